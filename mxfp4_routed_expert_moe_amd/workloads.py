@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for the MXFP4 routed-expert MoE layer.
+
+This module only draws inputs: random bf16 activations, an fp32 router matrix,
+random MXFP4 expert bytes in the canonical layout, a token-id hash table and the
+token ids, and it loads the stored per-expert selection bias of the Zipf
+workload.  It holds none of the layer's arithmetic (no routing, no decoding, no
+GEMM), so both the CPU oracle and the HIP path can take their inputs from it.
+
+Shapes follow the DeepSeek-V4-Flash MoE layer as the pages describe it
+("DeepSeek-V4-Flash export design", Source configuration, MoE bullet): hidden
+4096, 256 routed experts, top 6, intermediate 2048, one shared expert.
+
+Canonical MXFP4 layout of one projection with N output rows and K input
+columns (the reading of "ElytronAI / DeepSeek-v4-Flash", Sizes: an E2M1 nibble
+plane plus one E8M0 scale per 32 columns):
+  nibbles  uint8 [N, K/2]  byte b of row r holds column 2b in bits 3:0 and
+                           column 2b+1 in bits 7:4
+  scales   uint8 [N, K/32] E8M0 exponent of columns 32j .. 32j+31 of row r
+One canonical expert is gate [I,H] | up [I,H] | down [H,I], each projection
+stored as its nibble plane followed by its scale plane; experts follow each
+other with no padding, the shared expert last (index E).
+"""
+from __future__ import annotations
+
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HIDDEN = 4096
+INTER = 2048
+N_EXPERTS = 256
+TOP_K = 6
+ROUTE_SCALE = 1.5
+CLAMP_LIMIT = 10.0
+HASH_VOCAB = 65536
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_REPO = os.path.dirname(_HERE)
+ZIPF_BIAS_PATH = os.path.join(_REPO, "tests", "golden", "zipf_bias_e256.txt")
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    T: int
+    routing: str  # "learned" or "hash"
+    bias: str | None  # None or "zipf"
+
+    @property
+    def seed(self) -> int:
+        return 0x5EED0000 + self.index
+
+
+WORKLOADS = (
+    Workload(0, "decode_t4", 4, "learned", None),
+    Workload(1, "decode_t64", 64, "learned", None),
+    Workload(2, "hash_t256", 256, "hash", None),
+    Workload(3, "prefill_t4096", 4096, "learned", None),
+    Workload(4, "prefill_t16384_zipf", 16384, "learned", "zipf"),
+)
+
+
+# --------------------------------------------------------------------------
+# sizes of the canonical layout
+# --------------------------------------------------------------------------
+def projection_bytes(n_out: int, k_in: int) -> int:
+    """Bytes of one canonical MXFP4 projection: nibble plane + scale plane."""
+    return n_out * k_in // 2 + n_out * k_in // 32
+
+
+def expert_bytes(hidden: int, inter: int) -> int:
+    """Bytes of one canonical expert: gate [I,H], up [I,H], down [H,I]."""
+    return 2 * projection_bytes(inter, hidden) + projection_bytes(hidden, inter)
+
+
+def expert_plane_offsets(hidden: int, inter: int) -> dict:
+    """Byte offsets of the six planes inside one canonical expert."""
+    pg = projection_bytes(inter, hidden)
+    off = {}
+    off["gate_nib"] = 0
+    off["gate_sc"] = inter * hidden // 2
+    off["up_nib"] = pg
+    off["up_sc"] = pg + inter * hidden // 2
+    off["down_nib"] = 2 * pg
+    off["down_sc"] = 2 * pg + hidden * inter // 2
+    return off
+
+
+# --------------------------------------------------------------------------
+# generators
+# --------------------------------------------------------------------------
+def _rng(seed: int, *stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *stream])))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); uint16 bits.
+
+    Inputs here are finite normals from a Gaussian draw, so no NaN handling.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rnd = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + rnd) >> 16).astype(np.uint16)
+
+
+def make_x(seed: int, T: int, hidden: int = HIDDEN) -> np.ndarray:
+    """Activations: N(0,1) drawn in float32, rounded to bf16 -> uint16 [T, H]."""
+    g = _rng(seed, 1)
+    return f32_to_bf16_bits(g.standard_normal((T, hidden), dtype=np.float32))
+
+
+def make_router(seed: int, hidden: int = HIDDEN, n_experts: int = N_EXPERTS) -> np.ndarray:
+    """Router matrix W [H, E] float32 with entries N(0, 1/64)."""
+    g = _rng(seed, 2)
+    return (g.standard_normal((hidden, n_experts), dtype=np.float32) * np.float32(0.125)).astype(np.float32)
+
+
+def make_experts(seed: int, n_total: int, hidden: int = HIDDEN, inter: int = INTER,
+                 scale_lo: int = 118, scale_hi: int = 122) -> np.ndarray:
+    """Canonical MXFP4 blob of n_total experts (routed + shared), uint8.
+
+    Every E2M1 code is uniform over its 16 values (uniform random bytes give two
+    independent uniform nibbles) and every E8M0 scale byte is uniform over
+    [scale_lo, scale_hi], i.e. 2^U{-9..-5} for the default range.
+    Each expert draws from its own stream, so the blob is the same whatever
+    subset of it one later reads.
+    """
+    eb = expert_bytes(hidden, inter)
+    off = expert_plane_offsets(hidden, inter)
+    out = np.empty(n_total * eb, dtype=np.uint8)
+    nib_g = inter * hidden // 2
+    sc_g = inter * hidden // 32
+    nib_d = hidden * inter // 2
+    sc_d = hidden * inter // 32
+    for xid in range(n_total):
+        g = _rng(seed, 3, xid)
+        base = xid * eb
+        for name, nn, ns in (("gate", nib_g, sc_g), ("up", nib_g, sc_g), ("down", nib_d, sc_d)):
+            o = base + off[name + "_nib"]
+            out[o:o + nn] = np.frombuffer(g.bytes(nn), dtype=np.uint8)
+            o = base + off[name + "_sc"]
+            out[o:o + ns] = g.integers(scale_lo, scale_hi + 1, size=ns, dtype=np.uint8)
+    return out
+
+
+def make_hash(seed: int, T: int, n_experts: int = N_EXPERTS, top_k: int = TOP_K,
+              vocab: int = HASH_VOCAB):
+    """Token ids uniform over [0, vocab) and a table [vocab, top_k] int32 whose
+    rows are top_k distinct expert ids in random order (a uniformly random
+    partial permutation of 0..n_experts-1 per row)."""
+    g = _rng(seed, 4)
+    keys = g.random((vocab, n_experts), dtype=np.float32)
+    table = np.argsort(keys, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    tok = g.integers(0, vocab, size=T, dtype=np.int64).astype(np.int32)
+    return np.ascontiguousarray(table), tok
+
+
+def load_zipf_bias(n_experts: int = N_EXPERTS) -> np.ndarray:
+    """Per-expert selection bias of the Zipf(s=1.1) workload, float32 [E].
+
+    The stored values were written by tests/golden/make_zipf_bias.py, which
+    fits them with the CPU oracle's router on a separate calibration batch.
+    """
+    vals = []
+    with open(ZIPF_BIAS_PATH) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                vals.append(float(line))
+    b = np.asarray(vals, dtype=np.float32)
+    if b.shape != (n_experts,):
+        raise ValueError(f"{ZIPF_BIAS_PATH}: expected {n_experts} values, got {b.shape}")
+    return b
+
+
+@dataclass
+class LayerInputs:
+    workload: Workload
+    x: np.ndarray            # uint16 bf16 bits [T, H]
+    router: np.ndarray | None  # float32 [H, E]
+    bias: np.ndarray | None    # float32 [E]
+    table: np.ndarray | None   # int32 [V, k]
+    tok: np.ndarray | None     # int32 [T]
+    experts: np.ndarray        # uint8 canonical blob, (E + 1) experts
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+
+
+def make_layer_inputs(w: Workload, T: int | None = None, hidden: int = HIDDEN, inter: int = INTER,
+                      n_experts: int = N_EXPERTS, top_k: int = TOP_K, experts: np.ndarray | None = None) -> LayerInputs:
+    """All inputs of one workload (T may be overridden for a reduced sample)."""
+    T = w.T if T is None else T
+    x = make_x(w.seed, T, hidden)
+    router = bias = table = tok = None
+    if w.routing == "learned":
+        router = make_router(w.seed, hidden, n_experts)
+        if w.bias == "zipf":
+            bias = load_zipf_bias(n_experts)
+    else:
+        table, tok = make_hash(w.seed, T, n_experts, top_k)
+    if experts is None:
+        experts = make_experts(w.seed, n_experts + 1, hidden, inter)
+    return LayerInputs(w, x, router, bias, table, tok, experts, hidden, inter, n_experts, top_k)

@@ -1,0 +1,297 @@
+"""CPU oracle of the MXFP4 routed-expert MoE layer -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
+import or call this module.  The product path (the HIP library and its Python
+binding) never does, and this module shares no code with it: it has its own
+E2M1 table, its own reader of the canonical byte layout and its own loops.
+
+Plain and slow on purpose: numpy in float64, one expert at a time, no blocking
+or fusion.  A library matmul (numpy's float64 GEMM) serves as the dot-product
+step; every product of a bf16 activation and a decoded MXFP4 weight is exact in
+float64, so only the summation order differs from any other correct
+implementation.
+
+What the layer computes, with the passage each step follows:
+
+* Router ("Model techniques map -- DeepSeek-V4-Flash", Checked in its code,
+  rows "Mixture of experts" and "Auxiliary-loss-free load balancing";
+  "DeepSeek-V4-Flash export design", Source configuration, MoE bullet):
+  logits z = x W with the router kept in float32 storage, score
+  s = sqrt(softplus(z)), selection of the top 6 of s + b where the bias b only
+  changes which experts are chosen, weights gathered from the unbiased s,
+  normalised over the chosen six and scaled by 1.5.
+* Hash routing (same MoE bullet; "EasyDeL / DeepSeek-V4-Flash", Architecture):
+  the expert ids of a token are a row of a token-id table.
+* Experts (techniques map, row "SwiGLU feed-forward"): down(silu(min(gate(x), L))
+  * clamp(up(x), -L, L)); weights are MXFP4 ("ElytronAI / DeepSeek-v4-Flash",
+  Sizes: E2M1 codes with one E8M0 scale per group of 32 columns).
+* Shared expert and combine (techniques map, row "Shared expert"): the routed
+  outputs weighted and summed, plus the shared expert applied to the same input.
+
+Readings where the pages are silent (each also listed with the design notes):
+E2M1/E8M0 bit meaning per the OCP microscaling formats; low nibble = even
+column; scale groups run along the input (reduction) axis; ties in the top-6
+go to the lower expert id and the six come out in descending key order;
+softplus is the exact stable form; hash weights are 1.5/6; the shared expert
+has weight 1 and is stored as expert E; h = silu(.)*clamp(.) is rounded to
+bf16 before the down projection; dispatch order is (expert, token, slot).
+
+Parity status: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, brute force, invariants).  Full-layer outputs have no worked
+numeric example on the pages; they are pinned through those checks only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+# E2M1 code -> value: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0.
+# Codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6; codes 8..15 are their negatives.
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0], dtype=np.float64)
+
+
+def e8m0_value(e) -> np.ndarray:
+    """E8M0 scale byte -> 2^(e-127) in float64 (exact); 255 is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exact."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), returned
+    as float64.  Single rounding straight from float64, subnormals kept
+    (bf16 has 8 significant bits and the float32 exponent range)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    fin = np.isfinite(v)
+    a = np.abs(v[fin])
+    _, ex = np.frexp(a)             # a = m * 2^ex, m in [0.5, 1)
+    ex = np.maximum(ex, -125)       # below 2^-126 the quantum stays 2^-133
+    q = np.ldexp(1.0, ex - 8)       # spacing of 8-bit significands in [2^(ex-1), 2^ex)
+    r = np.rint(a / q) * q          # np.rint rounds half to even; a/q is exact
+    r = np.where(r >= 2.0 ** 128 - 2.0 ** 119, np.inf, r)  # beyond max bf16 rounds to inf
+    out[fin] = np.copysign(r, v[fin])
+    out[~fin] = v[~fin]
+    return out
+
+
+# --------------------------------------------------------------------------
+# canonical MXFP4 reader
+# --------------------------------------------------------------------------
+def decode_mxfp4(nibbles: np.ndarray, scales: np.ndarray, n_out: int, k_in: int) -> np.ndarray:
+    """Decode one canonical projection to float64 [n_out, k_in].
+
+    W[r, c] = E2M1(code of column c in row r) * 2^(scale[r, c // 32] - 127).
+    """
+    nib = np.asarray(nibbles, dtype=np.uint8).reshape(n_out, k_in // 2)
+    sc = np.asarray(scales, dtype=np.uint8).reshape(n_out, k_in // 32)
+    codes = np.empty((n_out, k_in), dtype=np.uint8)
+    codes[:, 0::2] = nib & 0x0F
+    codes[:, 1::2] = nib >> 4
+    w = E2M1_VALUES[codes].reshape(n_out, k_in // 32, 32)
+    w *= e8m0_value(sc)[:, :, None]
+    return w.reshape(n_out, k_in)
+
+
+def canonical_expert_size(hidden: int, inter: int) -> int:
+    """Bytes of one canonical expert (gate, up, down; 4.25 bits per weight)."""
+    proj = lambda n, k: n * k // 2 + n * k // 32  # noqa: E731
+    return 2 * proj(inter, hidden) + proj(hidden, inter)
+
+
+def decode_expert(blob: np.ndarray, xid: int, hidden: int, inter: int):
+    """Decode expert xid of a canonical blob -> (gate [I,H], up [I,H], down [H,I])."""
+    eb = canonical_expert_size(hidden, inter)
+    base = xid * eb
+    mats = []
+    pos = base
+    for n, k in ((inter, hidden), (inter, hidden), (hidden, inter)):
+        nn, ns = n * k // 2, n * k // 32
+        mats.append(decode_mxfp4(blob[pos:pos + nn], blob[pos + nn:pos + nn + ns], n, k))
+        pos += nn + ns
+    return tuple(mats)
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+def sqrt_softplus(z: np.ndarray) -> np.ndarray:
+    """s = sqrt(log(1 + e^z)) with the overflow-free form max(z,0) + log1p(e^-|z|)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.sqrt(np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z))))
+
+
+def router_logits(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """z[t, e] = sum_h x[t, h] * W[h, e], float64 products and sums."""
+    return bf16_bits_to_f64(x_bits) @ np.asarray(w_router, dtype=np.float32).astype(np.float64)
+
+
+def select_top_k(key: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest keys per row, descending; equal keys -> lower index
+    first (a stable sort of -key keeps the lower index ahead)."""
+    order = np.argsort(-key, axis=1, kind="stable")
+    return order[:, :k].astype(np.int32)
+
+
+def route_learned(x_bits, w_router, bias, top_k: int, route_scale: float):
+    """Learned routing -> (ids int32 [T,k], weights float64 [T,k], scores float64 [T,E])."""
+    z = router_logits(x_bits, w_router)
+    s = sqrt_softplus(z)
+    key = s if bias is None else s + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    ids = select_top_k(key, top_k)
+    sel = np.take_along_axis(s, ids.astype(np.int64), axis=1)
+    w = route_scale * sel / sel.sum(axis=1, keepdims=True)
+    return ids, w, s
+
+
+def route_hash(token_ids, table, top_k: int, route_scale: float):
+    """Hash routing: ids = table[token]; every weight route_scale / top_k."""
+    tok = np.asarray(token_ids, dtype=np.int64)
+    ids = np.asarray(table, dtype=np.int32)[tok, :top_k].copy()
+    w = np.full(ids.shape, route_scale / top_k, dtype=np.float64)
+    return ids, w
+
+
+def boundary_gap(x_bits, w_router, bias, top_k: int) -> np.ndarray:
+    """Per token, key[k-th] - key[(k+1)-th] (float64).  A tiny gap means the
+    selection sits on a near tie and either set is a correct answer."""
+    s = sqrt_softplus(router_logits(x_bits, w_router))
+    key = s if bias is None else s + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    part = -np.sort(-key, axis=1)
+    return part[:, top_k - 1] - part[:, top_k]
+
+
+# --------------------------------------------------------------------------
+# dispatch
+# --------------------------------------------------------------------------
+def dispatch(ids: np.ndarray, n_experts: int):
+    """Group the (token, slot) pairs by expert, stably in (expert, token, slot)
+    order, and append the shared-expert group (every token, in order).
+
+    Returns offsets int32 [E+2] (group g holds rows offsets[g]..offsets[g+1]-1,
+    group E is the shared expert), row_token int32 [rows] and slot_row int32
+    [T, k+1] (row of pair (t, j); column k is the shared row).  Ids outside
+    [0, E) are dropped: they get no row and slot_row -1.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    valid = (flat >= 0) & (flat < n_experts)
+    pair = np.nonzero(valid)[0]                       # (t, j) flat indices, ascending
+    order = pair[np.argsort(flat[pair], kind="stable")]
+    counts = np.bincount(flat[pair], minlength=n_experts)
+    offsets = np.zeros(n_experts + 2, dtype=np.int64)
+    offsets[1:n_experts + 1] = np.cumsum(counts)
+    n_routed = int(offsets[n_experts])
+    offsets[n_experts + 1] = n_routed + T
+    row_token = np.empty(n_routed + T, dtype=np.int64)
+    row_token[:n_routed] = order // k
+    row_token[n_routed:] = np.arange(T)
+    routed_row = np.full(T * k, -1, dtype=np.int64)
+    routed_row[order] = np.arange(n_routed)
+    slot_row = np.empty((T, k + 1), dtype=np.int64)
+    slot_row[:, :k] = routed_row.reshape(T, k)
+    slot_row[:, k] = n_routed + np.arange(T)
+    return offsets.astype(np.int32), row_token.astype(np.int32), slot_row.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# experts and combine
+# --------------------------------------------------------------------------
+def silu(v: np.ndarray) -> np.ndarray:
+    """silu(v) = v / (1 + e^-v) in float64."""
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu_clamped(g: np.ndarray, u: np.ndarray, limit: float) -> np.ndarray:
+    """silu(min(g, L)) * min(max(u, -L), L): gate clamped above only, up on both sides."""
+    return silu(np.minimum(g, limit)) * np.clip(u, -limit, limit)
+
+
+def expert_forward(xf: np.ndarray, mats, limit: float) -> np.ndarray:
+    """One expert on float64 rows xf [m, H] -> float64 [m, H]; h rounded to bf16."""
+    wg, wu, wd = mats
+    g = xf @ wg.T
+    u = xf @ wu.T
+    h = round_to_bf16(swiglu_clamped(g, u, limit))
+    return h @ wd.T
+
+
+def expert_ffn(x_bits, blob, offsets, row_token, limit: float, n_experts: int, hidden: int, inter: int,
+               groups=None) -> np.ndarray:
+    """Every dispatched row through its expert -> float64 [rows, H].
+
+    Expert-major: each group with rows is decoded once, then its rows run.
+    `groups` optionally restricts the work to some groups (other rows stay 0).
+    """
+    xf = bf16_bits_to_f64(x_bits)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    row_token = np.asarray(row_token, dtype=np.int64)
+    out = np.zeros((int(offsets[-1]), hidden), dtype=np.float64)
+    for g in (range(n_experts + 1) if groups is None else groups):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 == r0:
+            continue
+        mats = decode_expert(blob, g, hidden, inter)
+        out[r0:r1] = expert_forward(xf[row_token[r0:r1]], mats, limit)
+    return out
+
+
+def combine(out_rows: np.ndarray, slot_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """y[t] = sum_j w[t, j] * out[slot_row[t, j]] (j < k, in slot order) + out[shared row of t].
+
+    Slots whose row is -1 (dropped ids) contribute nothing.  float64."""
+    slot_row = np.asarray(slot_row, dtype=np.int64)
+    T, kp1 = slot_row.shape
+    k = kp1 - 1
+    H = out_rows.shape[1]
+    y = np.zeros((T, H), dtype=np.float64)
+    for j in range(k):
+        r = slot_row[:, j]
+        ok = r >= 0
+        y[ok] += np.asarray(weights, dtype=np.float64)[ok, j:j + 1] * out_rows[r[ok]]
+    y += out_rows[slot_row[:, k]]
+    return y
+
+
+def moe_layer(x_bits, blob, *, n_experts: int, hidden: int, inter: int, top_k: int,
+              route_scale: float, limit: float, w_router=None, bias=None, token_ids=None, table=None):
+    """The whole layer: route -> dispatch -> expert FFN -> combine.  Returns a dict
+    with ids, weights, offsets, row_token, slot_row, out_rows and y (float64)."""
+    if table is not None:
+        ids, w = route_hash(token_ids, table, top_k, route_scale)
+    else:
+        ids, w, _ = route_learned(x_bits, w_router, bias, top_k, route_scale)
+    offsets, row_token, slot_row = dispatch(ids, n_experts)
+    out = expert_ffn(x_bits, blob, offsets, row_token, limit, n_experts, hidden, inter)
+    y = combine(out, slot_row, w)
+    return dict(ids=ids, weights=w, offsets=offsets, row_token=row_token, slot_row=slot_row,
+                out_rows=out, y=y)
+
+
+def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, inter: int, limit: float):
+    """Brute force without dispatch: every token through ALL experts, masked by a
+    0/1 selection mask and weighted, plus the shared expert.  Tiny inputs only."""
+    xf = bf16_bits_to_f64(x_bits)
+    T = xf.shape[0]
+    ids = np.asarray(ids, dtype=np.int64)
+    y = np.zeros((T, hidden), dtype=np.float64)
+    for e in range(n_experts):
+        mask = (ids == e)                               # [T, k]
+        we = (np.asarray(weights, dtype=np.float64) * mask).sum(axis=1)  # 0 where not chosen
+        sel = mask.any(axis=1).astype(np.float64)
+        ye = expert_forward(xf, decode_expert(blob, e, hidden, inter), limit)
+        y += (sel * we)[:, None] * ye
+    y += expert_forward(xf, decode_expert(blob, n_experts, hidden, inter), limit)
+    return y

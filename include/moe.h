@@ -1,0 +1,216 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MXFP4 routed-expert MoE layer.
+ *
+ * One MoE layer of the DeepSeek-V4-Flash shape ("DeepSeek-V4-Flash export
+ * design", Source configuration, MoE bullet): hidden H = 4096, E = 256 routed
+ * experts, top k = 6, intermediate I = 2048, one shared expert, routing
+ * weights normalised and scaled by 1.5, or expert ids from a token-id hash
+ * table in the first layers.  The layer is four calls on one HIP stream:
+ *
+ *   moe_route       x -> (ids [T,k], weights [T,k])
+ *   moe_dispatch    ids -> (offsets, row_token, slot_row)
+ *   moe_expert_ffn  x, packed MXFP4 experts -> out_rows [rows, H] (float32)
+ *   moe_combine     out_rows, slot_row, weights -> y [T, H] (bf16)
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers unless a comment says host.  The caller owns
+ *    and allocates every buffer, workspaces included; the library never
+ *    allocates, frees, prints or aborts.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Each
+ *    call only enqueues kernels on it and returns; nothing synchronises.
+ *  - Arguments are validated on the host before anything is enqueued.  Any
+ *    return other than MOE_OK means nothing was enqueued.  MOE_EHIP means a
+ *    launch failed (hipGetLastError after the launches); work may have been
+ *    enqueued before the failing launch.
+ *  - T = 0 is a no-op that returns MOE_OK.
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Calls hold no state between them and may run from several host threads;
+ *    calls that share an output or workspace buffer on overlapping streams race.
+ *  - Results are deterministic: the same inputs give bit-identical outputs
+ *    (no floating-point atomics; every reduction runs in a fixed order).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1u
+
+/* Layout tags of an expert blob.  A blob whose tag is not the one a call
+ * expects is refused with MOE_ELAYOUT, so bytes in another layout are never
+ * misread (the "fail loudly" convention of "ElytronAI / DeepSeek-v4-Flash",
+ * Loading). */
+#define MOE_LAYOUT_CANONICAL_MXFP4 0x4D584330u  /* host reference layout, below */
+#define MOE_LAYOUT_GFX950_TILED_V1 0x4D584731u  /* device layout read by the kernels */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,      /* NULL pointer, negative size, inconsistent arguments */
+  MOE_EALIGN = 2,      /* a pointer misses its required alignment */
+  MOE_ELAYOUT = 3,     /* wrong layout tag or ABI version in a descriptor */
+  MOE_ESHAPE = 4,      /* unsupported H, I, E or top_k, or expert_bytes mismatch */
+  MOE_EWORKSPACE = 5,  /* workspace smaller than the matching *_workspace_size() */
+  MOE_EHIP = 6         /* a HIP launch failed */
+} moe_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_str(int status);
+
+/* Library ABI version (MOE_ABI_VERSION of the build). */
+uint32_t moe_abi_version(void);
+
+/*
+ * Expert weights: MXFP4 ("ElytronAI / DeepSeek-v4-Flash", Sizes): every
+ * weight is an E2M1 code (sign, 2 exponent bits with bias 1, 1 mantissa bit:
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) times the E8M0 scale 2^(e-127) of
+ * its group of 32 consecutive input columns.  4.25 bits per weight, no
+ * padding.  The experts of a layer sit back to back in one blob with no gap,
+ * so expert xid starts at base + xid * expert_bytes (same page, Layout); the
+ * shared expert is stored as xid = n_experts.
+ *
+ * Canonical layout of one expert (host side, the input of moe_pack_mxfp4):
+ *   gate [I, H] | up [I, H] | down [H, I]; each projection [N, K] is its
+ *   nibble plane uint8 [N][K/2] (byte b of a row: column 2b in bits 3:0,
+ *   column 2b+1 in bits 7:4) followed by its scale plane uint8 [N][K/32].
+ *
+ * Device layout MOE_LAYOUT_GFX950_TILED_V1: the same six planes at the same
+ * offsets with the bytes of each plane permuted (a pure permutation, so
+ * expert_bytes is unchanged):
+ *   nibble plane: 1024-byte tiles t = (n/16) * (K/128) + (k/128); inside a
+ *     tile, lane l = 16*g + r (r < 16, g < 4) owns bytes [16l, 16l+16): the
+ *     canonical bytes of row 16*(n/16) + r covering columns
+ *     128*(k/128) + 32*g .. +31, in canonical nibble order.
+ *   scale plane: 256-byte blocks b = (n/16) * (K/512) + (k/512); byte 4l+i of
+ *     a block is the scale of row 16*(n/16) + (l%16) for the 32-column group
+ *     16*(k/512) + 4*i + (l/16).
+ * One 64-lane wave reads a tile with one coalesced 16-byte load per lane and
+ * holds exactly the 32 codes, and the one scale, that its MFMA fragments need.
+ */
+typedef struct moe_experts {
+  uint32_t abi_version;   /* MOE_ABI_VERSION */
+  uint32_t layout;        /* MOE_LAYOUT_GFX950_TILED_V1 for the compute calls */
+  int32_t n_experts;      /* routed experts E (blob holds E + 1 experts) */
+  int32_t hidden;         /* H */
+  int32_t inter;          /* I */
+  int32_t reserved;       /* must be 0 */
+  uint64_t expert_bytes;  /* must equal moe_expert_bytes(H, I) */
+  const void* base;       /* device pointer, 256-byte aligned */
+} moe_experts;
+
+/* Bytes of one expert (gate + up + down) of shape (H, I): 3*H*I*17/32.
+ * Returns 0 for unsupported shapes (H, I must be positive multiples of 512). */
+uint64_t moe_expert_bytes(int32_t hidden, int32_t inter);
+
+/* Fill a descriptor for a device blob in MOE_LAYOUT_GFX950_TILED_V1.
+ * MOE_EINVAL for NULL d/base, MOE_ESHAPE for an unsupported shape or E. */
+int moe_experts_init(moe_experts* d, const void* base, int32_t n_experts, int32_t hidden, int32_t inter);
+
+/*
+ * Host-side repack canonical -> device layout (and back), for n_total experts
+ * (routed + shared) of shape (H, I).  src and dst are HOST pointers to
+ * n_total * moe_expert_bytes(H, I) bytes each (dst_bytes/src_bytes must be at
+ * least that), and must not overlap.  The repack is a pure byte permutation,
+ * so unpack(pack(b)) == b exactly (the round trip that "ElytronAI /
+ * DeepSeek-v4-Flash", Verification, reports for its own repacked blobs).
+ * Synchronous; touches no GPU.
+ */
+int moe_pack_mxfp4(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_total, int32_t hidden,
+                   int32_t inter, uint8_t* dst_device_layout, uint64_t dst_bytes);
+int moe_unpack_mxfp4(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_total, int32_t hidden,
+                     int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes);
+
+/*
+ * Routing ("Model techniques map -- DeepSeek-V4-Flash", Checked in its code,
+ * rows "Mixture of experts" and "Auxiliary-loss-free load balancing";
+ * "DeepSeek-V4-Flash export design", Source configuration, MoE bullet).
+ *
+ * Learned mode (hash_table == NULL):
+ *   z[t,e] = sum_h x[t,h] * w_router[h,e]   accumulated in float64
+ *   s      = sqrt(softplus(z))              float64
+ *   ids[t] = the top_k experts by s + sel_bias[e] (sel_bias NULL = 0), in
+ *            descending key order, equal keys to the lower expert id
+ *   weights[t,j] = route_scale * s[ids[t,j]] / sum_j s[ids[t,j]]  (unbiased s)
+ * Hash mode (hash_table != NULL): ids[t,j] = hash_table[token_ids[t]*top_k + j]
+ *   and weights = route_scale / top_k.  A token id outside [0, V) gives ids -1
+ *   for that token (moe_dispatch then drops those pairs).
+ *
+ * x        bf16 [T, H] row-major, 16-byte aligned
+ * w_router float32 [H, E] row-major (learned mode)
+ * sel_bias float32 [E] or NULL
+ * token_ids int32 [T], hash_table int32 [V, top_k] (hash mode)
+ * ids      int32 [T, top_k] out;  weights float32 [T, top_k] out
+ * ws       device workspace of at least moe_route_workspace_size(T, H, E) bytes,
+ *          256-byte aligned (learned mode; may be NULL in hash mode)
+ * Requirements: 1 <= top_k <= 8, top_k <= E <= 256, H a positive multiple of 512.
+ */
+size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E);
+int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, const float* sel_bias,
+              const int32_t* token_ids, const int32_t* hash_table, int32_t V, int32_t E, int32_t top_k,
+              float route_scale, int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch: groups the (token, slot) pairs by expert for the experts call
+ * ("Model techniques map -- DeepSeek-V4-Flash", row "Shared expert": the
+ * experts module takes the flattened tokens with the routed ids and weights).
+ * Rows are ordered by (expert, token, slot) -- a stable counting sort -- and
+ * the shared-expert group (every token, in order) comes last.
+ *
+ * ids       int32 [T, top_k] in
+ * offsets   int32 [E + 2] out: group g (g < E routed, g = E shared) owns rows
+ *           offsets[g] .. offsets[g+1]-1; offsets[E+1] = total rows
+ * row_token int32 [T * (top_k + 1)] out: token of each row
+ * slot_row  int32 [T, top_k + 1] out: row of pair (t, j); column top_k is the
+ *           shared-expert row of t
+ * Ids outside [0, E) get no row and slot_row -1 (they contribute nothing).
+ * ws: at least moe_dispatch_workspace_size(T, E, top_k) bytes, 256-byte aligned.
+ */
+size_t moe_dispatch_workspace_size(int32_t T, int32_t E, int32_t top_k);
+int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_t* offsets, int32_t* row_token,
+                 int32_t* slot_row, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFN over every dispatched row ("Model techniques map --
+ * DeepSeek-V4-Flash", row "SwiGLU feed-forward"; clamping also named in
+ * "DeepSeek-V4-Flash export design", V3 reuse and V4 differences):
+ *   g = W_gate[e] x,  u = W_up[e] x                  (float32 accumulation)
+ *   h = bf16( silu(min(g, L)) * min(max(u, -L), L) )
+ *   out_rows[p] = W_down[e] h                        (float32 accumulation)
+ * for each row p of group e, x = x[row_token[p]].  The MXFP4 weights are
+ * decoded to bf16 on the fly and fed to bf16 MFMA; only the experts that own
+ * rows are read.
+ *
+ * x         bf16 [T, H]; experts: descriptor (host pointer) of the device blob
+ * offsets, row_token: as written by moe_dispatch for the same T, E, top_k
+ * out_rows  float32 [T * (top_k + 1), H] out (rows past offsets[E+1] untouched)
+ * ws        at least moe_ffn_workspace_size(T, experts, top_k) bytes, 256-byte aligned
+ * clamp_limit L > 0.
+ */
+size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k);
+int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
+                   const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weighted combine plus the shared expert ("Model techniques map --
+ * DeepSeek-V4-Flash", row "Shared expert"):
+ *   y[t] = bf16( sum_{j<top_k} weights[t,j] * out_rows[slot_row[t,j]]
+ *                + out_rows[slot_row[t,top_k]] )
+ * summed in float32 in that fixed order (the deterministic reduction the
+ * techniques map lists under inference kernels).  slot_row entries of -1 are
+ * skipped.
+ * out_rows float32 [rows, H]; slot_row int32 [T, top_k+1]; weights float32
+ * [T, top_k]; y bf16 [T, H] out.  H a positive multiple of 8.
+ */
+int moe_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
+                int32_t top_k, uint16_t* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

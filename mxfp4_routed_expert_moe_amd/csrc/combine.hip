@@ -1,0 +1,67 @@
+// Weighted combine of the routed expert rows plus the shared expert
+// ("Model techniques map -- DeepSeek-V4-Flash", row "Shared expert": the
+// routed output is added to the shared expert of the same input):
+//   y[t] = bf16( sum_{j<k} w[t,j] * out[slot_row[t,j]] + out[slot_row[t,k]] )
+// A plain gather-reduce in a fixed order -- no atomics -- so the output is
+// bit-reproducible (the deterministic reductions listed among the inference
+// kernels of the same page).  HBM bound: each thread owns 8 columns of one
+// token, reads 7 rows of 32 bytes and writes 16 bytes.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out_rows,
+                                                      const int32_t* __restrict__ slot_row,
+                                                      const float* __restrict__ weights, int T, int H, int k,
+                                                      uint16_t* __restrict__ y) {
+  const int groups = H >> 3;
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const int t = static_cast<int>(idx / groups);
+  const int c = static_cast<int>(idx % groups) * 8;
+  if (t >= T) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  const int32_t* sr = slot_row + static_cast<size_t>(t) * (k + 1);
+  for (int j = 0; j < k; ++j) {
+    const int r = sr[j];
+    if (r < 0) continue;
+    const float w = weights[static_cast<size_t>(t) * k + j];
+    const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(r) * H + c);
+    const f32x4 v0 = p[0], v1 = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = fmaf(w, v0[i], acc[i]);
+      acc[4 + i] = fmaf(w, v1[i], acc[4 + i]);
+    }
+  }
+  {
+    const int r = sr[k];
+    const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(r) * H + c);
+    const f32x4 v0 = p[0], v1 = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += v0[i];
+      acc[4 + i] += v1[i];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = static_cast<uint32_t>(float_to_bf16_bits(acc[2 * i])) |
+           (static_cast<uint32_t>(float_to_bf16_bits(acc[2 * i + 1])) << 16);
+  *reinterpret_cast<u32x4*>(y + static_cast<size_t>(t) * H + c) = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
+                          uint16_t* y, hipStream_t s) {
+  const long threads = static_cast<long>(T) * (H / 8);
+  combine_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, s>>>(out_rows, slot_row, weights, T, H, k, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

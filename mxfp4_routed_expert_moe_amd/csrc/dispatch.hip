@@ -1,0 +1,137 @@
+// Dispatch of the MoE layer: a stable counting sort of the (token, slot)
+// pairs by expert, followed by the shared-expert group of every token in
+// order.  The experts call of the DeepSeek-V4-Flash sparse block takes the
+// flattened tokens together with the routed ids ("Model techniques map --
+// DeepSeek-V4-Flash", row "Shared expert"); the row order chosen here,
+// (expert, token, slot), makes every later step deterministic.
+//
+// Three kernels, no host synchronisation and no ordering atomics:
+//  1. per chunk of 32 tokens: the rank of each pair among the earlier pairs
+//     of the chunk with the same expert, and the chunk's per-expert counts;
+//  2. per expert (one wave): exclusive scan of its counts over the chunks;
+//  3. per chunk: exclusive scan of the expert totals -> offsets, then every
+//     pair's row = offsets[e] + chunk base + rank, and the shared rows.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kChunk = 32;  // tokens per chunk
+
+struct DispatchWs {
+  int32_t* rank;   // [T*k]
+  int32_t* cnt;    // [E][nch] counts, then exclusive chunk bases
+  int32_t* total;  // [E]
+};
+
+__host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+__host__ __device__ inline DispatchWs carve(void* ws, int T, int E, int k) {
+  const int nch = (T + kChunk - 1) / kChunk;
+  char* p = static_cast<char*>(ws);
+  DispatchWs w;
+  w.rank = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * static_cast<size_t>(T) * k);
+  w.cnt = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * static_cast<size_t>(E) * nch);
+  w.total = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                            int nch, DispatchWs w) {
+  __shared__ int sid[kChunk * 8];
+  __shared__ int hist[1024];
+  const int c = blockIdx.x;
+  const int t0 = c * kChunk;
+  const int n = min(kChunk, T - t0) * k;
+  for (int i = threadIdx.x; i < E; i += 256) hist[i] = 0;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int e = ids[static_cast<size_t>(t0) * k + i];
+    sid[i] = (e >= 0 && e < E) ? e : -1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const int e = sid[i];
+    if (e < 0) continue;
+    int r = 0;
+    for (int j = 0; j < i; ++j) r += (sid[j] == e) ? 1 : 0;
+    w.rank[static_cast<size_t>(t0) * k + i] = r;
+    atomicAdd(&hist[e], 1);  // integer counts: the result does not depend on order
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += 256) w.cnt[static_cast<size_t>(i) * nch + c] = hist[i];
+}
+
+// grid E, 64 threads: exclusive scan of cnt[e][0..nch) in place, total[e].
+__global__ __launch_bounds__(64) void dispatch_chunk_scan_kernel(int nch, DispatchWs w) {
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x;
+  int32_t* row = w.cnt + static_cast<size_t>(e) * nch;
+  int carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nch ? row[c] : 0;
+    const int incl = wave_incl_scan(v);
+    if (c < nch) row[c] = carry + incl - v;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) w.total[e] = carry;
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                               int nch, DispatchWs w, int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ row_token,
+                                                               int32_t* __restrict__ slot_row) {
+  __shared__ int off[1024];
+  __shared__ int tmp[4];
+  for (int i = threadIdx.x; i < E; i += 256) off[i] = w.total[i];
+  __syncthreads();
+  const int n_routed = block_excl_scan_256(off, E, tmp);
+  const int c = blockIdx.x;
+  if (c == 0) {
+    for (int i = threadIdx.x; i < E; i += 256) offsets[i] = off[i];
+    if (threadIdx.x == 0) {
+      offsets[E] = n_routed;
+      offsets[E + 1] = n_routed + T;
+    }
+  }
+  const int t0 = c * kChunk;
+  const int nt = min(kChunk, T - t0);
+  for (int i = threadIdx.x; i < nt * k; i += 256) {
+    const int t = t0 + i / k, j = i % k;
+    const int e = ids[static_cast<size_t>(t0) * k + i];
+    int32_t row = -1;
+    if (e >= 0 && e < E) {
+      row = off[e] + w.cnt[static_cast<size_t>(e) * nch + c] + w.rank[static_cast<size_t>(t0) * k + i];
+      row_token[row] = t;
+    }
+    slot_row[static_cast<size_t>(t) * (k + 1) + j] = row;
+  }
+  for (int i = threadIdx.x; i < nt; i += 256) {
+    const int t = t0 + i;
+    row_token[n_routed + t] = t;
+    slot_row[static_cast<size_t>(t) * (k + 1) + k] = n_routed + t;
+  }
+}
+
+}  // namespace
+
+size_t dispatch_ws_bytes(int T, int E, int k) {
+  const int nch = (T + kChunk - 1) / kChunk;
+  return align256(sizeof(int32_t) * static_cast<size_t>(T) * k) +
+         align256(sizeof(int32_t) * static_cast<size_t>(E) * nch) + align256(sizeof(int32_t) * static_cast<size_t>(E));
+}
+
+hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
+                           int32_t* slot_row, void* ws, hipStream_t s) {
+  const int nch = (T + kChunk - 1) / kChunk;
+  DispatchWs w = carve(ws, T, E, k);
+  dispatch_rank_kernel<<<nch, 256, 0, s>>>(ids, T, E, k, nch, w);
+  dispatch_chunk_scan_kernel<<<E, 64, 0, s>>>(nch, w);
+  dispatch_scatter_kernel<<<nch, 256, 0, s>>>(ids, T, E, k, nch, w, offsets, row_token, slot_row);
+  return hipGetLastError();
+}
+
+}  // namespace moe

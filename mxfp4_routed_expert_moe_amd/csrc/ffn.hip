@@ -1,0 +1,432 @@
+// Expert FFN of the MoE layer on gfx950: for every dispatched row p of group
+// e (E routed experts, then the shared expert),
+//   h = bf16( silu(min(W_gate[e] x, L)) * clamp(W_up[e] x, -L, L) )
+//   out_rows[p] = W_down[e] h
+// ("Model techniques map -- DeepSeek-V4-Flash", row "SwiGLU feed-forward";
+// weights MXFP4 as in "ElytronAI / DeepSeek-v4-Flash", Sizes).
+//
+// MXFP4 bytes stream from HBM in the tiled device layout: one 16-byte load per
+// lane gives the 32 codes of one column for one 128-wide k tile, and the
+// hardware scaled convert turns 8 codes and their E8M0 scale into the 8 bf16
+// of one 16x16x32 MFMA B fragment.  Nothing is ever dequantised to memory.
+//
+// Work is a device-side list of items (group, first row, row count) built
+// from the dispatch offsets, so the host never learns the per-expert counts:
+// the grid covers the worst case and surplus blocks return at once.
+//
+// Two kernel families:
+//  * decode (few rows per expert, HBM bound): the four waves of a block split
+//    the K axis and share one set of 16-row tiles; each wave streams its
+//    quarter of the block's weight columns with 16-byte loads one k tile
+//    ahead, and the partial sums meet in LDS in a fixed order;
+//  * prefill (many rows per expert, MFMA bound): 128-row tiles of the
+//    gathered activations go through LDS (row pitch padded so that MFMA
+//    fragment reads are bank-conflict free), double buffered; each wave owns
+//    a 64 x 64 output tile and reads its weight fragments straight from HBM.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPrefillRows = 128;
+constexpr int kLdsPitch = 136;  // bf16 per LDS row: 128 + 8 of padding (272 bytes)
+
+__host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+struct FfnWs {
+  int32_t* n_items;  // [1]
+  int4* items;       // [max_items]
+  uint16_t* h;       // [rows, I] bf16
+};
+
+inline int ffn_max_items(int T, int E, int k, int bm) {
+  const long rows = static_cast<long>(T) * (k + 1);
+  return static_cast<int>((rows + bm - 1) / bm) + E + 1;
+}
+
+inline FfnWs ffn_carve(void* ws, int max_items) {
+  char* p = static_cast<char*>(ws);
+  FfnWs w;
+  w.n_items = reinterpret_cast<int32_t*>(p);
+  p += 256;
+  w.items = reinterpret_cast<int4*>(p);
+  p += align256(sizeof(int4) * static_cast<size_t>(max_items));
+  w.h = reinterpret_cast<uint16_t*>(p);
+  return w;
+}
+
+// Work list: every group with rows is cut into items of at most bm rows.
+__global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets, int E, int bm,
+                                                       int4* __restrict__ items, int32_t* __restrict__ n_items) {
+  __shared__ int cnt[1024];
+  __shared__ int tmp[4];
+  const int G = E + 1;
+  for (int g = threadIdx.x; g < G; g += 256) {
+    const int c = offsets[g + 1] - offsets[g];
+    cnt[g] = (c + bm - 1) / bm;
+  }
+  __syncthreads();
+  const int total = block_excl_scan_256(cnt, G, tmp);
+  for (int g = threadIdx.x; g < G; g += 256) {
+    const int r0 = offsets[g];
+    const int c = offsets[g + 1] - r0;
+    const int base = cnt[g];
+    for (int i = 0; i * bm < c; ++i) items[base + i] = make_int4(g, r0 + i * bm, min(bm, c - i * bm), 0);
+  }
+  if (threadIdx.x == 0) *n_items = total;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// ------------------------------------------------------------------ decode
+// grid (n blocks, max items), 256 threads.  GATEUP: 64 output columns per
+// block (4 gate + 4 up n-tiles), K = H, A = x rows via row_token, output h.
+// Otherwise: 128 output columns (8 down n-tiles), K = I, A = h rows, output
+// float32 rows.  MT 16-row m-tiles per item (rows <= 16*MT).
+template <int MT, bool GATEUP>
+__global__ __launch_bounds__(256) void ffn_decode_kernel(const uint16_t* __restrict__ act,
+                                                         const int32_t* __restrict__ row_token,
+                                                         const int4* __restrict__ items,
+                                                         const int32_t* __restrict__ n_items,
+                                                         const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                         int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                         float* __restrict__ out_rows) {
+  const int item = blockIdx.y;
+  if (item >= *n_items) return;
+  const int4 it = items[item];
+  const int g = it.x, row0 = it.y, nrows = it.z;
+  const int K = GATEUP ? H : I;
+  const int KT = K >> 7;
+  const int KTW = KT >> 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kt0 = wave * KTW;
+  const ExpertPlanes pl = expert_planes(H, I);
+  const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+
+  const uint8_t* nib[8];
+  const uint8_t* scl[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int nt;
+    uint64_t onib, osc;
+    if (GATEUP) {
+      nt = blockIdx.x * 4 + (j & 3);
+      onib = j < 4 ? pl.gate_nib : pl.up_nib;
+      osc = j < 4 ? pl.gate_sc : pl.up_sc;
+    } else {
+      nt = blockIdx.x * 8 + j;
+      onib = pl.down_nib;
+      osc = pl.down_sc;
+    }
+    nib[j] = eb + onib + static_cast<uint64_t>(nt) * KT * 1024 + lane * 16;
+    scl[j] = eb + osc + static_cast<uint64_t>(nt) * (KT >> 2) * 256 + lane * 4;
+  }
+
+  const int mtiles = (nrows + 15) >> 4;
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = mt * 16 + (lane & 15);
+    arow[mt] = nullptr;
+    if (r < nrows) {
+      const int p = row0 + r;
+      arow[mt] = GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I;
+      arow[mt] += 32 * (lane >> 4);
+    }
+  }
+
+  f32x4 acc[MT][8];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 bq[8], bn[8];
+  uint32_t sw[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bq[j] = ld16(nib[j] + static_cast<size_t>(kt0) * 1024);
+
+  for (int kt = kt0; kt < kt0 + KTW; ++kt) {
+    if (kt + 1 < kt0 + KTW) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bn[j] = ld16(nib[j] + static_cast<size_t>(kt + 1) * 1024);
+    }
+    if (kt == kt0 || (kt & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sw[j] = *reinterpret_cast<const uint32_t*>(scl[j] + static_cast<size_t>(kt >> 2) * 256);
+    }
+    u32x4 a[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < mtiles) {
+        if (arow[mt]) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[mt][q] = ld16(arow[mt] + kt * 128 + 8 * q);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[mt][q] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    float scf[8];
+    const int sh = 8 * (kt & 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) scf[j] = e8m0_to_float((sw[j] >> sh) & 255u);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 b = dequant8(bq[j][s], scf[j]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          if (mt < mtiles) acc[mt][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mt][s]), b, acc[mt][j]);
+      }
+    }
+    if (kt + 1 < kt0 + KTW) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bq[j] = bn[j];
+    }
+  }
+
+  // Split-K partial sums meet in LDS; summed in wave order 0,1,2,3.
+  __shared__ f32x4 red[4][8][64];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt >= mtiles) break;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[mt][j];
+    __syncthreads();
+    const int rbase = mt * 16 + 4 * (lane >> 4);
+    if (GATEUP) {
+      const int jg = wave, ju = 4 + wave;
+      const f32x4 gs = ((red[0][jg][lane] + red[1][jg][lane]) + red[2][jg][lane]) + red[3][jg][lane];
+      const f32x4 us = ((red[0][ju][lane] + red[1][ju][lane]) + red[2][ju][lane]) + red[3][ju][lane];
+      const int col = blockIdx.x * 64 + wave * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rbase + i;
+        if (r < nrows) {
+          const float gv = fminf(gs[i], limit);
+          const float uv = fminf(fmaxf(us[i], -limit), limit);
+          h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * wave + jj;
+        const f32x4 os = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+        const int col = blockIdx.x * 128 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + i;
+          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = os[i];
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+// grid (n blocks, max items), 256 threads = 2 x 2 waves, 128-row items.
+// GATEUP: 64 output columns per block (wave column wn: gate and up n-tiles of
+// output columns 32*wn .. 32*wn+31).  Otherwise 128 output columns per block
+// (wave column wn: 4 down n-tiles).
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const int4* __restrict__ items,
+                                                             const int32_t* __restrict__ n_items,
+                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                             int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                             float* __restrict__ out_rows) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kPrefillRows * kLdsPitch];
+  const int item = blockIdx.y;
+  if (item >= *n_items) return;
+  const int4 it = items[item];
+  const int g = it.x, row0 = it.y, nrows = it.z;
+  const int K = GATEUP ? H : I;
+  const int KT = K >> 7;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const ExpertPlanes pl = expert_planes(H, I);
+  const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+
+  const uint8_t* nib[4];
+  const uint8_t* scl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int nt;
+    uint64_t onib, osc;
+    if (GATEUP) {
+      nt = blockIdx.x * 4 + wn * 2 + (j & 1);
+      onib = j < 2 ? pl.gate_nib : pl.up_nib;
+      osc = j < 2 ? pl.gate_sc : pl.up_sc;
+    } else {
+      nt = blockIdx.x * 8 + wn * 4 + j;
+      onib = pl.down_nib;
+      osc = pl.down_sc;
+    }
+    nib[j] = eb + onib + static_cast<uint64_t>(nt) * KT * 1024 + lane * 16;
+    scl[j] = eb + osc + static_cast<uint64_t>(nt) * (KT >> 2) * 256 + lane * 4;
+  }
+
+  // A loader: 16 threads per row (16 bytes each = one 128-wide k tile row),
+  // rows tid/16 + 16*q.
+  const int lc = tid & 15, lr = tid >> 4;
+  const uint16_t* ldp[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = lr + 16 * q;
+    ldp[q] = nullptr;
+    if (r < nrows) {
+      const int p = row0 + r;
+      ldp[q] = (GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I) + lc * 8;
+    }
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 areg[8];
+  u32x4 bq[4], bn[4];
+  uint32_t sw[4];
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) areg[q] = ldp[q] ? ld16(ldp[q] + kt * 128) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<u32x4*>(&As[buf][(lr + 16 * q) * kLdsPitch + lc * 8]) = areg[q];
+  };
+
+  load_a(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bq[j] = ld16(nib[j]);
+  store_a(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const bool more = kt + 1 < KT;
+    if (more) {
+      load_a(kt + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bn[j] = ld16(nib[j] + static_cast<size_t>(kt + 1) * 1024);
+    }
+    if ((kt & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sw[j] = *reinterpret_cast<const uint32_t*>(scl[j] + static_cast<size_t>(kt >> 2) * 256);
+    }
+    float scf[4];
+    const int sh = 8 * (kt & 3);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scf[j] = e8m0_to_float((sw[j] >> sh) & 255u);
+    const uint16_t* abase = &As[kt & 1][(wm * 64 + (lane & 15)) * kLdsPitch + 32 * (lane >> 4)];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = dequant8(bq[j][s], scf[j]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mt * 16 * kLdsPitch + 8 * s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16x16x32(a, b[j], acc[mt][j]);
+      }
+    }
+    if (more) {
+      store_a((kt + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bq[j] = bn[j];
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int rbase = wm * 64 + mt * 16 + 4 * (lane >> 4);
+    if (GATEUP) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = blockIdx.x * 64 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + i;
+          if (r < nrows) {
+            const float gv = fminf(acc[mt][j][i], limit);
+            const float uv = fminf(fmaxf(acc[mt][j + 2][i], -limit), limit);
+            h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = blockIdx.x * 128 + wn * 64 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rbase + i;
+          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = acc[mt][j][i];
+        }
+      }
+    }
+  }
+}
+
+// Rows per item of the decode kernels (16 * MT) for a given T.
+inline int decode_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+
+// Decode kernels while the average group holds at most ~16 rows.
+inline bool use_decode(int T, int E, int k) { return static_cast<long>(T) * (k + 1) <= 16L * (E + 1); }
+
+template <int MT>
+hipError_t launch_decode(const uint16_t* x, const uint8_t* blob, uint64_t eb, int H, int I, const int32_t* row_token,
+                         float limit, float* out_rows, const FfnWs& w, int max_items, hipStream_t s) {
+  dim3 g1(I / 64, max_items), g2(H / 128, max_items);
+  ffn_decode_kernel<MT, true><<<g1, 256, 0, s>>>(x, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h, nullptr);
+  ffn_decode_kernel<MT, false><<<g2, 256, 0, s>>>(w.h, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
+                                                  out_rows);
+  return hipGetLastError();
+}
+
+inline int ffn_bm(int T, int E, int k) { return use_decode(T, E, k) ? 16 * decode_mt(T) : kPrefillRows; }
+
+}  // namespace
+
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k) {
+  (void)H;
+  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k));
+  return 256 + align256(sizeof(int4) * static_cast<size_t>(mi)) +
+         align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
+}
+
+hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
+                      int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
+                      void* ws, hipStream_t s) {
+  const int bm = ffn_bm(T, E, k);
+  const int max_items = ffn_max_items(T, E, k, bm);
+  FfnWs w = ffn_carve(ws, max_items);
+  ffn_plan_kernel<<<1, 256, 0, s>>>(offsets, E, bm, w.items, w.n_items);
+  if (use_decode(T, E, k)) {
+    switch (decode_mt(T)) {
+      case 1: return launch_decode<1>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
+      case 2: return launch_decode<2>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
+      default: return launch_decode<4>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
+    }
+  }
+  dim3 g1(I / 64, max_items), g2(H / 128, max_items);
+  ffn_prefill_kernel<true><<<g1, 256, 0, s>>>(x, row_token, w.items, w.n_items, blob, expert_bytes, H, I, limit, w.h,
+                                              nullptr);
+  ffn_prefill_kernel<false><<<g2, 256, 0, s>>>(w.h, nullptr, w.items, w.n_items, blob, expert_bytes, H, I, limit,
+                                               nullptr, out_rows);
+  return hipGetLastError();
+}
+
+}  // namespace moe

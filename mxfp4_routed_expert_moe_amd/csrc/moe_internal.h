@@ -1,0 +1,145 @@
+// Internal declarations of the gfx950 MoE library: device helpers shared by the
+// kernels and the launch functions that moe_api.hip calls after validating.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- MXFP4
+// E8M0 scale byte -> float32 2^(e-127): e = 0 is the subnormal 2^-127 and
+// e = 255 is NaN (OCP microscaling E8M0).
+__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
+  uint32_t bits = e << 23;
+  bits = (e == 0u) ? 0x00400000u : bits;
+  bits = (e == 255u) ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
+}
+
+// Eight E2M1 codes (one 32-bit word, low nibble first) times one scale ->
+// eight bf16 in k order, the B operand of one 16x16x32 bf16 MFMA.  The
+// hardware convert is exact here: an E2M1 value times a power of two has two
+// significant bits.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
+  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  u32x4 w;
+  w[0] = __builtin_bit_cast(uint32_t, p0);
+  w[1] = __builtin_bit_cast(uint32_t, p1);
+  w[2] = __builtin_bit_cast(uint32_t, p2);
+  w[3] = __builtin_bit_cast(uint32_t, p3);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Byte offsets of the six planes inside one expert (same in both layouts).
+struct ExpertPlanes {
+  uint64_t gate_nib, gate_sc, up_nib, up_sc, down_nib, down_sc;
+};
+
+__host__ __device__ inline ExpertPlanes expert_planes(int H, int I) {
+  const uint64_t nh = static_cast<uint64_t>(H) * I;
+  ExpertPlanes p;
+  p.gate_nib = 0;
+  p.gate_sc = nh / 2;
+  p.up_nib = nh / 2 + nh / 32;
+  p.up_sc = p.up_nib + nh / 2;
+  p.down_nib = 2 * (nh / 2 + nh / 32);
+  p.down_sc = p.down_nib + nh / 2;
+  return p;
+}
+
+__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+
+// ---------------------------------------------------------------- wave / block scans
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive scan of n <= 1024 ints in LDS buffer `a` (in place) by a 256-thread
+// block; returns the total to every thread.  `tmp` needs 4 ints.
+__device__ inline int block_excl_scan_256(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    v[i] = idx < n ? a[idx] : 0;
+    local += v[i];
+  }
+  const int incl = wave_incl_scan(local);
+  const int wave = tid >> 6;
+  if ((tid & 63) == 63) tmp[wave] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  for (int w = 0; w < wave; ++w) wave_base += tmp[w];
+  const int total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  int run = wave_base + incl - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    if (idx < n) a[idx] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipGetLastError() of its launches.  Arguments are validated
+// by the caller in moe_api.hip.
+int route_hsplit(int T, int H);
+hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w, const float* bias, int E, int k,
+                                float scale, int32_t* ids, float* weights, double* part, hipStream_t s);
+hipError_t launch_route_hash(const int32_t* tok, int T, const int32_t* table, int V, int k, float scale,
+                             int32_t* ids, float* weights, hipStream_t s);
+
+size_t dispatch_ws_bytes(int T, int E, int k);
+hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
+                           int32_t* slot_row, void* ws, hipStream_t s);
+
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k);
+hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
+                      int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
+                      void* ws, hipStream_t s);
+
+hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
+                          uint16_t* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,102 @@
+// Host repack of MXFP4 expert blobs: canonical layout <-> gfx950 tiled layout.
+//
+// Both layouts hold the same six planes (gate, up, down nibbles and scales) at
+// the same offsets; the tiled layout permutes the bytes inside each plane so
+// that a 64-lane wave loads one 16-column x 128-k tile with one coalesced
+// 16-byte load per lane, and the E8M0 scales of four such tiles with one
+// 4-byte load per lane.  Being a permutation, the repack keeps the byte count
+// (the repacking "ElytronAI / DeepSeek-v4-Flash" describes under Sizes keeps
+// its expert payload byte-identical in size, and its Verification section
+// reports exact inversion).
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+
+namespace {
+
+bool shape_ok(int32_t H, int32_t I) { return H > 0 && I > 0 && H % 512 == 0 && I % 512 == 0; }
+
+// Offset in the tiled nibble plane of canonical byte (n, kb) of an [N, K] projection.
+inline uint64_t tiled_nib_index(int N, int K, int n, int kb) {
+  (void)N;
+  const int k = kb * 2;
+  const int tile = (n / 16) * (K / 128) + k / 128;
+  const int lane = 16 * ((k % 128) / 32) + n % 16;
+  return static_cast<uint64_t>(tile) * 1024 + lane * 16 + (kb % 16);
+}
+
+// Offset in the tiled scale plane of canonical scale (n, grp) of an [N, K] projection.
+inline uint64_t tiled_sc_index(int N, int K, int n, int grp) {
+  (void)N;
+  const int block = (n / 16) * (K / 512) + grp / 16;
+  const int i = (grp % 16) / 4;  // k tile within the 512 block
+  const int gq = grp % 4;        // 32-column group within the k tile
+  const int lane = 16 * gq + n % 16;
+  return static_cast<uint64_t>(block) * 256 + lane * 4 + i;
+}
+
+// dir = +1: canonical -> tiled; -1: tiled -> canonical.
+void permute_projection(const uint8_t* src, uint8_t* dst, int N, int K, int dir) {
+  const int kbytes = K / 2;
+  for (int n = 0; n < N; ++n) {
+    for (int kb = 0; kb < kbytes; kb += 16) {
+      const uint64_t c = static_cast<uint64_t>(n) * kbytes + kb;
+      const uint64_t t = tiled_nib_index(N, K, n, kb);
+      if (dir > 0) memcpy(dst + t, src + c, 16);
+      else memcpy(dst + c, src + t, 16);
+    }
+  }
+  const uint64_t nib_bytes = static_cast<uint64_t>(N) * K / 2;
+  const int groups = K / 32;
+  for (int n = 0; n < N; ++n) {
+    for (int gi = 0; gi < groups; ++gi) {
+      const uint64_t c = nib_bytes + static_cast<uint64_t>(n) * groups + gi;
+      const uint64_t t = nib_bytes + tiled_sc_index(N, K, n, gi);
+      if (dir > 0) dst[t] = src[c];
+      else dst[c] = src[t];
+    }
+  }
+}
+
+int repack(const uint8_t* src, uint64_t src_bytes, int32_t n_total, int32_t H, int32_t I, uint8_t* dst,
+           uint64_t dst_bytes, int dir) {
+  if (!src || !dst) return MOE_EINVAL;
+  if (n_total <= 0) return MOE_EINVAL;
+  if (!shape_ok(H, I)) return MOE_ESHAPE;
+  const uint64_t eb = moe_expert_bytes(H, I);
+  const uint64_t need = eb * static_cast<uint64_t>(n_total);
+  if (src_bytes < need || dst_bytes < need) return MOE_EINVAL;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + need && b < a + need) return MOE_EINVAL;  // overlapping buffers
+  const uint64_t pg = static_cast<uint64_t>(I) * H / 2 + static_cast<uint64_t>(I) * H / 32;
+  for (int32_t x = 0; x < n_total; ++x) {
+    const uint8_t* s = src + eb * x;
+    uint8_t* d = dst + eb * x;
+    permute_projection(s, d, I, H, dir);                    // gate [I, H]
+    permute_projection(s + pg, d + pg, I, H, dir);          // up   [I, H]
+    permute_projection(s + 2 * pg, d + 2 * pg, H, I, dir);  // down [H, I]
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t moe_expert_bytes(int32_t hidden, int32_t inter) {
+  if (!shape_ok(hidden, inter)) return 0;
+  return 3ull * static_cast<uint64_t>(hidden) * static_cast<uint64_t>(inter) * 17ull / 32ull;
+}
+
+int moe_pack_mxfp4(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_total, int32_t hidden, int32_t inter,
+                   uint8_t* dst_device_layout, uint64_t dst_bytes) {
+  return repack(src_canonical, src_bytes, n_total, hidden, inter, dst_device_layout, dst_bytes, +1);
+}
+
+int moe_unpack_mxfp4(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_total, int32_t hidden,
+                     int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes) {
+  return repack(src_device_layout, src_bytes, n_total, hidden, inter, dst_canonical, dst_bytes, -1);
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+"""GPU parity of the MoE layer against the CPU oracle, through the C ABI.
+
+Small shapes run the whole layer element by element (several tiles, ragged
+tails, both expert-FFN kernel families, empty experts); the five full-size
+workloads check routing and dispatch on every token and the expert rows and
+outputs on sampled tokens, in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import moe_oracle as O  # noqa: E402
+from mxfp4_routed_expert_moe_amd import binding as B  # noqa: E402
+from mxfp4_routed_expert_moe_amd import workloads as WL  # noqa: E402
+from tests import layer_check as LC  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _small_inputs(T, hidden, inter, E, seed, routing="learned", bias=False):
+    w = WL.Workload(90, "small", T, routing, None)
+    x = WL.make_x(seed, T, hidden)
+    router = b = table = tok = None
+    if routing == "learned":
+        router = WL.make_router(seed, hidden, E)
+        if bias:
+            b = (np.random.default_rng(seed).standard_normal(E) * 0.5).astype(np.float32)
+    else:
+        table, tok = WL.make_hash(seed, T, E, 6, vocab=1000)
+    experts = WL.make_experts(seed, E + 1, hidden, inter)
+    return WL.LayerInputs(w, x, router, b, table, tok, experts, hidden, inter, E, 6)
+
+
+def _experts(inp):
+    return B.Experts.from_canonical(inp.experts, inp.n_experts, inp.hidden, inp.inter)
+
+
+# T*7 <= 16*(E+1) selects the decode kernels, above it the prefill kernels.
+SMALL = [
+    # (T, H, I, E, routing, bias)
+    (1, 512, 512, 16, "learned", False),      # decode, one m-tile, 1 row per expert
+    (5, 512, 1024, 16, "learned", False),     # decode, MT=1
+    (29, 1024, 512, 32, "learned", True),     # decode, MT=2, selection bias
+    (37, 512, 512, 16, "learned", False),     # decode, MT=4 (shared group spans 3 m-tiles)
+    (61, 512, 512, 16, "hash", False),        # hash routing
+    (300, 512, 512, 16, "learned", False),    # prefill, ragged 128-row tiles
+    (700, 512, 512, 256, "learned", False),   # prefill, 256 experts, many tiny groups
+    (64, 512, 512, 256, "learned", True),     # decode with 256 experts, many empty
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,routing,bias", SMALL)
+def test_layer_small_shapes(T, H, I, E, routing, bias):
+    print(f"[parity] small T={T} H={H} I={I} E={E} {routing} bias={bias}", flush=True)
+    inp = _small_inputs(T, H, I, E, 1000 + T, routing, bias)
+    r = LC.full_check(inp, _experts(inp))
+    assert r["ambiguous"] == 0
+    # every row, not just a sample: compare all expert rows too
+    g = r["g"]
+    ref = O.moe_layer(inp.x, inp.experts, n_experts=E, hidden=H, inter=I, top_k=6, route_scale=1.5,
+                      limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table)
+    n = int(ref["offsets"][-1])
+    LC.assert_output_close(LC.host(g["out_rows"][:n]), ref["out_rows"], "all rows")
+    LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
+
+
+def test_determinism_bitwise():
+    inp = _small_inputs(300, 512, 512, 16, 77)
+    ex = _experts(inp)
+    a = LC.run_gpu_layer(inp, ex)
+    b = LC.run_gpu_layer(inp, ex)
+    assert np.array_equal(a["y"], b["y"])
+    assert torch.equal(a["out_rows"], b["out_rows"])
+    inp2 = _small_inputs(40, 512, 512, 16, 78)
+    ex2 = _experts(inp2)
+    assert np.array_equal(LC.run_gpu_layer(inp2, ex2)["y"], LC.run_gpu_layer(inp2, ex2)["y"])
+
+
+@pytest.mark.parametrize("T", [3, 200])
+def test_down_exponent_plus_one_doubles_bitwise(T):
+    # a power-of-two rescale of every down weight doubles each expert row exactly
+    inp = _small_inputs(T, 512, 512, 16, 55)
+    ex1 = _experts(inp)
+    blob2 = inp.experts.copy()
+    eb = WL.expert_bytes(512, 512)
+    off = WL.expert_plane_offsets(512, 512)
+    for xid in range(17):
+        s0 = xid * eb + off["down_sc"]
+        blob2[s0:s0 + 512 * 512 // 32] += 1
+    ex2 = B.Experts.from_canonical(blob2, 16, 512, 512)
+    a = LC.run_gpu_layer(inp, ex1)
+    b = LC.run_gpu_layer(inp, ex2)
+    n = int(a["offsets"][-1])
+    assert torch.equal(b["out_rows"][:n], 2 * a["out_rows"][:n])
+
+
+def _identity_blob(hidden, inter, n_total, up_code):
+    eb = WL.expert_bytes(hidden, inter)
+    off = WL.expert_plane_offsets(hidden, inter)
+    blob = np.zeros(n_total * eb, dtype=np.uint8)
+    for xid in range(n_total):
+        b = xid * eb
+        for name, code in (("gate", 0x2), ("up", up_code)):
+            nib = blob[b + off[name + "_nib"]: b + off[name + "_nib"] + inter * hidden // 2].reshape(inter, hidden // 2)
+            i = np.arange(inter)
+            nib[i, i // 2] |= (code << (4 * (i & 1))).astype(np.uint8)
+            blob[b + off[name + "_sc"]: b + off[name + "_sc"] + inter * hidden // 32] = 127
+        nib = blob[b + off["down_nib"]: b + off["down_nib"] + hidden * inter // 2].reshape(hidden, inter // 2)
+        i = np.arange(inter)
+        nib[i, i // 2] |= (0x2 << (4 * (i & 1))).astype(np.uint8)
+        blob[b + off["down_sc"]: b + off["down_sc"] + hidden * inter // 32] = 127
+    return blob
+
+
+@pytest.mark.parametrize("T", [4, 300])
+def test_identity_experts_closed_form_and_orientation(T):
+    # gate = I, up = 2I, down = I: every expert row is silu(min(x,L)) * clamp(2x,-L,L)
+    # in its first I columns and 0 beyond; a swapped gate/up would differ.
+    H, I, E, L = 1024, 512, 16, WL.CLAMP_LIMIT
+    inp = _small_inputs(T, H, I, E, 91)
+    xf = np.random.default_rng(5).standard_normal((T, H)).astype(np.float32) * 4
+    xf[0, :6] = [12.0, -12.0, 9.99, -9.99, 10.0, -10.0]
+    inp.x = WL.f32_to_bf16_bits(xf)
+    blob = _identity_blob(H, I, E + 1, 0x4)
+    inp.experts = blob
+    g = LC.run_gpu_layer(inp, B.Experts.from_canonical(blob, E, H, I))
+    rows = LC.host(g["out_rows"][: int(g["offsets"][-1])]).astype(np.float64)
+    v = O.bf16_bits_to_f64(inp.x)[g["row_token"][: rows.shape[0]], :I]
+    silu = lambda a: a / (1 + np.exp(-a))  # noqa: E731
+    want = silu(np.minimum(v, L)) * np.clip(2 * v, -L, L)
+    # h is rounded to bf16 (half an ulp: 2^-8 relative); the fp32 SiLU adds ~1e-6
+    assert np.all(np.abs(rows[:, :I] - want) <= 2.0 ** -8 * (1 + 1e-4) * np.abs(want) + 1e-30)
+    assert np.all(rows[:, I:] == 0)
+    swapped = silu(np.minimum(2 * v, L)) * np.clip(v, -L, L)
+    assert np.mean(np.abs(rows[:, :I] - swapped)) > 0.1
+
+
+def test_edge_cases_empty_and_dropped_ids():
+    H, I, E = 512, 512, 16
+    inp = _small_inputs(9, H, I, E, 12)
+    ex = _experts(inp)
+    layer = B.MoeLayer(ex, 9, 6, 1.5, WL.CLAMP_LIMIT, w_router=LC.dev(inp.router))
+    # T = 0 is a no-op through every call
+    assert B.lib().moe_combine(None, None, None, 0, H, 6, None, None) == 0
+    # dispatch + ffn + combine with ids containing out-of-range values: they are dropped
+    ids = np.stack([np.random.default_rng(i).permutation(E)[:6] for i in range(9)]).astype(np.int32)
+    ids[2, 1] = E + 5
+    ids[4, 0] = -7
+    layer.ids.copy_(LC.dev(ids))
+    layer.weights.fill_(0.25)
+    layer.dispatch()
+    xd = LC.dev(inp.x)
+    layer.expert_ffn(xd)
+    layer.combine()
+    torch.cuda.synchronize()
+    off, rt, sr = O.dispatch(ids, E)
+    assert np.array_equal(LC.host(layer.offsets), off)
+    assert np.array_equal(LC.host(layer.slot_row), sr)
+    assert np.array_equal(LC.host(layer.row_token)[: off[-1]], rt)
+    out = O.expert_ffn(inp.x, inp.experts, off, rt, WL.CLAMP_LIMIT, E, H, I)
+    y = O.combine(out, sr, np.full((9, 6), 0.25))
+    LC.assert_output_close(O.bf16_bits_to_f64(LC.host(layer.y).view(np.uint16)), y, "dropped ids")
+
+
+def test_hash_out_of_range_token_gives_dropped_ids():
+    E = 16
+    table, tok = WL.make_hash(3, 10, E, 6, vocab=50)
+    tok[3] = 50
+    tok[7] = -1
+    ids, w = B.route(None, 10, E, 6, 1.5, token_ids=LC.dev(tok), hash_table=LC.dev(table))
+    ids = LC.host(ids)
+    assert np.all(ids[3] == -1) and np.all(ids[7] == -1)
+    ok = [t for t in range(10) if t not in (3, 7)]
+    assert np.array_equal(ids[ok], table[tok[ok]])
+    assert np.all(LC.host(w) == 0.25)
+
+
+# ---------------------------------------------------------------- full-size workloads
+_EXPERTS_CACHE = {}
+
+
+def _full_inputs(index):
+    w = WL.WORKLOADS[index]
+    if w.seed not in _EXPERTS_CACHE:
+        _EXPERTS_CACHE.clear()
+        canon = WL.make_experts(w.seed, WL.N_EXPERTS + 1)
+        _EXPERTS_CACHE[w.seed] = (canon, B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER))
+    canon, ex = _EXPERTS_CACHE[w.seed]
+    return WL.make_layer_inputs(w, experts=canon), ex
+
+
+@pytest.mark.parametrize("index,sample", [(0, None), (1, 12), (2, 12), (3, 8), (4, 8)])
+def test_full_workloads(index, sample):
+    w = WL.WORKLOADS[index]
+    print(f"[parity] full workload {w.name} T={w.T}", flush=True)
+    inp, ex = _full_inputs(index)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index)
+    print(f"[parity] {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}, ambiguous {r['ambiguous']}", flush=True)
+    if index == 4:
+        counts = np.diff(r["g"]["offsets"][: WL.N_EXPERTS + 1])
+        assert counts.max() >= 0.98 * w.T              # the hottest expert takes nearly every token
+        assert np.median(counts) < 200
+    del r
+    torch.cuda.empty_cache()

@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 routed-expert MoE layer on one MI355X.
+
+One step is the whole layer -- moe_route, moe_dispatch, the three launches of
+moe_expert_ffn and moe_combine -- over one batch of the workload's seeded
+synthetic inputs, already resident in HBM.  The expert blob is held in four
+copies at different addresses and the steps rotate through them, so the
+256 MB last-level cache cannot serve one step's expert bytes to the next.
+
+Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
+kernel (the expert gate/up launch: HBM-bound for the decode workloads, MFMA
+for prefill), timed with HIP events on the library's stream, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode_t64]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
+FFN_SRC = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc", "ffn.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_t64")
+    p.add_argument("--copies", type=int, default=4, help="expert blob copies rotated across steps")
+    p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="run one device copy of this size first (to scale HBM counters)")
+    return p.parse_args()
+
+
+def ffn_source_hash() -> str:
+    with open(FFN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str, bytes_alg_per_launch: float):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when none exists or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"ffn_gateup_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("ffn_source_sha256_16") != ffn_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, n_tokens: int):
+    """The oracle as it stands, on the first n_tokens of the workload."""
+    import numpy as np
+    from oracle import moe_oracle as O
+    from mxfp4_routed_expert_moe_amd import workloads as WL
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    S = min(n_tokens, inp.x.shape[0])
+    t0 = time.perf_counter()
+    r = O.moe_layer(inp.x[:S], inp.experts, n_experts=inp.n_experts, hidden=inp.hidden, inter=inp.inter,
+                    top_k=inp.top_k, route_scale=WL.ROUTE_SCALE, limit=WL.CLAMP_LIMIT, w_router=inp.router,
+                    bias=inp.bias, token_ids=None if inp.tok is None else inp.tok[:S], table=inp.table)
+    dt = time.perf_counter() - t0
+    n_exp = int(np.count_nonzero(np.diff(r["offsets"])))
+    return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {S} of {inp.x.shape[0]} tokens of {inp.workload.name}: full layer, "
+                       f"{n_exp} experts decoded, {dt:.1f} s wall; float64 numpy, BLAS threads={cores}")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mxfp4_routed_expert_moe_amd import binding as B
+    from mxfp4_routed_expert_moe_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fail loudly if the library is missing
+    wl = {w.name: w for w in WL.WORKLOADS}[args.workload]
+    print(f"[bench] workload {wl.name} T={wl.T}: generating inputs", file=sys.stderr, flush=True)
+    inp = WL.make_layer_inputs(wl)
+    H, I, E, k, T = inp.hidden, inp.inter, inp.n_experts, inp.top_k, wl.T
+
+    dev = torch.device("cuda", 0)
+    if args.calib_copy_mib > 0:
+        # an elementwise kernel that reads n bytes and writes n bytes
+        n = (args.calib_copy_mib << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty(n, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+
+    packed = B.pack_mxfp4(inp.experts, E + 1, H, I)
+    blob0 = torch.from_numpy(packed).to(dev)
+    del packed
+    blobs = [blob0] + [blob0.clone() for _ in range(args.copies - 1)]
+    experts = [B.Experts(b, E, H, I) for b in blobs]
+    to_dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    layer = B.MoeLayer(experts[0], T, k, WL.ROUTE_SCALE, WL.CLAMP_LIMIT, w_router=to_dev(inp.router),
+                       sel_bias=to_dev(inp.bias), hash_table=to_dev(inp.table))
+    x = to_dev(inp.x.view(np.int16))
+    tok = to_dev(inp.tok)
+    torch.cuda.synchronize()
+
+    K, W = args.steps, args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+
+    def step(i, timed):
+        layer.set_experts(experts[i % len(experts)])
+        layer.route(x, tok)
+        layer.dispatch()
+        layer.expert_ffn_phase(x, 0)
+        if timed:
+            ev[i][0].record()
+        layer.expert_ffn_phase(x, 1)
+        if timed:
+            ev[i][1].record()
+        layer.expert_ffn_phase(x, 2)
+        if timed:
+            ev[i][2].record()
+        layer.combine()
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for i in range(W):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / K
+    value = T * K / elapsed
+    gateup_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    down_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+
+    # algorithmic work of the gate/up launch, from this run's own ids
+    ids = layer.ids.cpu().numpy()
+    used = int(len(np.unique(ids[(ids >= 0) & (ids < E)]))) + 1   # + the shared expert
+    rows = int(layer.offsets[-1].item())
+    proj_bytes = H * I * 17 // 32
+    gateup_bytes = used * 2 * proj_bytes + rows * H * 2 + rows * I * 2
+    gateup_flops = rows * 2 * 2 * H * I
+    decode = rows <= 16 * (E + 1)
+    if decode:
+        achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+        traffic = read_traffic(wl.name, gateup_bytes)
+    else:
+        achieved = gateup_flops / (gateup_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4))
+        traffic = read_traffic(wl.name, gateup_bytes)
+    roof["traffic"] = traffic
+    roof["kernel"] = "ffn gate/up (moe_expert_ffn phase 1)"
+    roof["avg_launch_us"] = round(gateup_ms * 1e3, 2)
+    roof["algorithmic_bytes_per_launch"] = gateup_bytes
+    roof["algorithmic_flops_per_launch"] = gateup_flops
+
+    layer_bytes = used * 3 * proj_bytes
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
+                   "routing": wl.routing, "bias": wl.bias, "weights": "mxfp4 e2m1+e8m0/32",
+                   "experts_read_per_step": used, "expert_bytes_per_step": layer_bytes,
+                   "blob_copies_rotated": len(experts)},
+        "roofline": roof,
+        "layer_hbm_gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "stages_us": {"ffn_gateup": round(gateup_ms * 1e3, 2), "ffn_down": round(down_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

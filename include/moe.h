@@ -196,6 +196,18 @@ int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same expert FFN enqueued one launch at a time, for callers that time or
+ * interleave the launches: phase 0 builds the work list from offsets, phase 1
+ * runs gate/up + clamped SwiGLU into the workspace (h, bf16), phase 2 runs
+ * the down projection into out_rows.  Phases 0, 1, 2 issued in order on one
+ * stream with identical arguments (same workspace) equal one moe_expert_ffn
+ * call bit for bit.  phase -1 runs all three; any other value is MOE_EINVAL.
+ */
+int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
+                         const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
+                         void* ws, size_t ws_bytes, int32_t phase, void* stream);
+
+/*
  * Weighted combine plus the shared expert ("Model techniques map --
  * DeepSeek-V4-Flash", row "Shared expert"):
  *   y[t] = bf16( sum_{j<top_k} weights[t,j] * out_rows[slot_row[t,j]]

@@ -25,7 +25,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "M
 
 EXPORTED = ("moe_status_str", "moe_abi_version", "moe_expert_bytes", "moe_experts_init", "moe_pack_mxfp4",
             "moe_unpack_mxfp4", "moe_route_workspace_size", "moe_route", "moe_dispatch_workspace_size",
-            "moe_dispatch", "moe_ffn_workspace_size", "moe_expert_ffn", "moe_combine")
+            "moe_dispatch", "moe_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_phase", "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "moe_ffn_workspace_size": (c_sz, [c_i32, ctypes.POINTER(moe_experts), c_i32]),
         "moe_expert_ffn": (ctypes.c_int, [vp, c_i32, ctypes.POINTER(moe_experts), c_i32, vp, vp, ctypes.c_float,
                                           vp, vp, c_sz, vp]),
+        "moe_expert_ffn_phase": (ctypes.c_int, [vp, c_i32, ctypes.POINTER(moe_experts), c_i32, vp, vp,
+                                                ctypes.c_float, vp, vp, c_sz, c_i32, vp]),
         "moe_combine": (ctypes.c_int, [vp, vp, vp, c_i32, c_i32, c_i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -272,6 +274,11 @@ class MoeLayer:
                                                       _ptr(self.offsets), _ptr(self.row_token), self.limit,
                                                       _ptr(self.out_rows), _ptr(self.ws_ffn), self.ws_ffn.numel(),
                                                       _stream()))
+
+    def expert_ffn_phase(self, x, phase: int):
+        _check("moe_expert_ffn_phase", lib().moe_expert_ffn_phase(
+            _ptr(x), self.T, ctypes.byref(self.experts.desc), self.k, _ptr(self.offsets), _ptr(self.row_token),
+            self.limit, _ptr(self.out_rows), _ptr(self.ws_ffn), self.ws_ffn.numel(), phase, _stream()))
 
     def combine(self):
         _check("moe_combine", lib().moe_combine(_ptr(self.out_rows), _ptr(self.slot_row), _ptr(self.weights),

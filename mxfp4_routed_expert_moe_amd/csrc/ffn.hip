@@ -80,150 +80,144 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // ------------------------------------------------------------------ decode
-// grid (n blocks, max items), 256 threads.  GATEUP: 64 output columns per
-// block (4 gate + 4 up n-tiles), K = H, A = x rows via row_token, output h.
-// Otherwise: 128 output columns (8 down n-tiles), K = I, A = h rows, output
-// float32 rows.  MT 16-row m-tiles per item (rows <= 16*MT).
-template <int MT, bool GATEUP>
-__global__ __launch_bounds__(256) void ffn_decode_kernel(const uint16_t* __restrict__ act,
-                                                         const int32_t* __restrict__ row_token,
-                                                         const int4* __restrict__ items,
-                                                         const int32_t* __restrict__ n_items,
-                                                         const uint8_t* __restrict__ blob, uint64_t expert_bytes,
-                                                         int H, int I, float limit, uint16_t* __restrict__ h_out,
-                                                         float* __restrict__ out_rows) {
+// grid (n blocks, max items), 256 threads, items of at most 16 rows.
+// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles), K = H, A = x
+// rows via row_token, output h.  Otherwise 128 output columns (8 down
+// n-tiles), K = I, A = h rows, output float32 rows.  Wave w owns k tiles
+// [w*KTW, (w+1)*KTW) of all 8 n-tiles.  The k loop is fully unrolled over a
+// ring of three register buffers, so two k tiles (8 KB per wave) of weight
+// loads stay in flight while one is consumed; the activation loads of a tile
+// are issued one tile ahead and before the weight loads two tiles ahead, so
+// the in-order load counter never makes a tile wait for a later one.
+template <bool GATEUP, int KTW>
+__global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
+                                                            const int32_t* __restrict__ row_token,
+                                                            const int4* __restrict__ items,
+                                                            const int32_t* __restrict__ n_items,
+                                                            const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                            int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                            float* __restrict__ out_rows) {
+  constexpr int KT = 4 * KTW;        // k tiles of the whole K axis
+  constexpr int NSW = KTW >= 4 ? KTW / 4 : 1;  // scale words per n-tile per wave
   const int item = blockIdx.y;
   if (item >= *n_items) return;
   const int4 it = items[item];
   const int g = it.x, row0 = it.y, nrows = it.z;
-  const int K = GATEUP ? H : I;
-  const int KT = K >> 7;
-  const int KTW = KT >> 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kt0 = wave * KTW;
   const ExpertPlanes pl = expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+  constexpr uint64_t kTileStride = static_cast<uint64_t>(KT) * 1024;  // bytes between n-tiles
+  constexpr uint64_t kScStride = static_cast<uint64_t>(KT / 4) * 256;
 
-  const uint8_t* nib[8];
-  const uint8_t* scl[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int nt;
-    uint64_t onib, osc;
-    if (GATEUP) {
-      nt = blockIdx.x * 4 + (j & 3);
-      onib = j < 4 ? pl.gate_nib : pl.up_nib;
-      osc = j < 4 ? pl.gate_sc : pl.up_sc;
-    } else {
-      nt = blockIdx.x * 8 + j;
-      onib = pl.down_nib;
-      osc = pl.down_sc;
-    }
-    nib[j] = eb + onib + static_cast<uint64_t>(nt) * KT * 1024 + lane * 16;
-    scl[j] = eb + osc + static_cast<uint64_t>(nt) * (KT >> 2) * 256 + lane * 4;
+  const uint8_t* nb0;
+  const uint8_t* nb1;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  if (GATEUP) {
+    nb0 = eb + pl.gate_nib + blockIdx.x * 4 * kTileStride;
+    nb1 = eb + pl.up_nib + blockIdx.x * 4 * kTileStride;
+    sb0 = eb + pl.gate_sc + blockIdx.x * 4 * kScStride;
+    sb1 = eb + pl.up_sc + blockIdx.x * 4 * kScStride;
+  } else {
+    nb0 = eb + pl.down_nib + blockIdx.x * 8 * kTileStride;
+    nb1 = nb0 + 4 * kTileStride;
+    sb0 = eb + pl.down_sc + blockIdx.x * 8 * kScStride;
+    sb1 = sb0 + 4 * kScStride;
   }
+  nb0 += static_cast<uint64_t>(kt0) * 1024 + lane * 16;
+  nb1 += static_cast<uint64_t>(kt0) * 1024 + lane * 16;
+  sb0 += static_cast<uint64_t>(kt0 >> 2) * 256 + lane * 4;
+  sb1 += static_cast<uint64_t>(kt0 >> 2) * 256 + lane * 4;
 
-  const int mtiles = (nrows + 15) >> 4;
-  const uint16_t* arow[MT];
+  // Padded lanes (rows >= nrows) re-read the item's last row; their results
+  // are never stored.
+  const int r = lane & 15;
+  const int p = row0 + min(r, nrows - 1);
+  const uint16_t* arow = (GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I) +
+                         32 * (lane >> 4) + kt0 * 128;
+
+  uint32_t sw[NSW][8];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = mt * 16 + (lane & 15);
-    arow[mt] = nullptr;
-    if (r < nrows) {
-      const int p = row0 + r;
-      arow[mt] = GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I;
-      arow[mt] += 32 * (lane >> 4);
-    }
+  for (int d = 0; d < NSW; ++d)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sw[d][j] = *reinterpret_cast<const uint32_t*>((j < 4 ? sb0 : sb1) + (j & 3) * kScStride + d * 256);
+
+  u32x4 bq[3][8];
+  u32x4 a[2][4];
+  auto load_b = [&](int buf, int i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[buf][j] = ld16((j < 4 ? nb0 : nb1) + (j & 3) * kTileStride + i * 1024);
+  };
+  auto load_a = [&](int buf, int i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[buf][q] = ld16(arow + i * 128 + 8 * q);
+  };
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0, 0);
+  load_b(0, 0);
+  if (KTW > 1) {
+    load_a(1, 1);
+    load_b(1, 1);
   }
-
-  f32x4 acc[MT][8];
+  // sched_barrier(0) keeps the compiler from sinking prefetches below the
+  // MFMAs of the current tile (which would leave one tile in flight).
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 bq[8], bn[8];
-  uint32_t sw[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) bq[j] = ld16(nib[j] + static_cast<size_t>(kt0) * 1024);
-
-  for (int kt = kt0; kt < kt0 + KTW; ++kt) {
-    if (kt + 1 < kt0 + KTW) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bn[j] = ld16(nib[j] + static_cast<size_t>(kt + 1) * 1024);
-    }
-    if (kt == kt0 || (kt & 3) == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sw[j] = *reinterpret_cast<const uint32_t*>(scl[j] + static_cast<size_t>(kt >> 2) * 256);
-    }
-    u32x4 a[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt < mtiles) {
-        if (arow[mt]) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) a[mt][q] = ld16(arow[mt] + kt * 128 + 8 * q);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) a[mt][q] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    float scf[8];
+  for (int i = 0; i < KTW; ++i) {
+    if (i + 2 < KTW) load_b((i + 2) % 3, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kt = kt0 + i;
     const int sh = 8 * (kt & 3);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) scf[j] = e8m0_to_float((sw[j] >> sh) & 255u);
+    const int d = KTW >= 4 ? (i >> 2) : 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const bf16x8 b = dequant8(bq[j][s], scf[j]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (mt < mtiles) acc[mt][j] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[mt][s]), b, acc[mt][j]);
+        const float sc = e8m0_to_float((sw[d][j] >> sh) & 255u);
+        acc[j] = mfma16x16x32(av, dequant8(bq[i % 3][j][s], sc), acc[j]);
       }
     }
-    if (kt + 1 < kt0 + KTW) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) bq[j] = bn[j];
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < KTW) load_a(i & 1, i + 2);
   }
 
   // Split-K partial sums meet in LDS; summed in wave order 0,1,2,3.
   __shared__ f32x4 red[4][8][64];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= mtiles) break;
-    __syncthreads();
+  for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  const int rbase = 4 * (lane >> 4);
+  if (GATEUP) {
+    const int jg = wave, ju = 4 + wave;
+    const f32x4 gs = ((red[0][jg][lane] + red[1][jg][lane]) + red[2][jg][lane]) + red[3][jg][lane];
+    const f32x4 us = ((red[0][ju][lane] + red[1][ju][lane]) + red[2][ju][lane]) + red[3][ju][lane];
+    const int col = blockIdx.x * 64 + wave * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[mt][j];
-    __syncthreads();
-    const int rbase = mt * 16 + 4 * (lane >> 4);
-    if (GATEUP) {
-      const int jg = wave, ju = 4 + wave;
-      const f32x4 gs = ((red[0][jg][lane] + red[1][jg][lane]) + red[2][jg][lane]) + red[3][jg][lane];
-      const f32x4 us = ((red[0][ju][lane] + red[1][ju][lane]) + red[2][ju][lane]) + red[3][ju][lane];
-      const int col = blockIdx.x * 64 + wave * 16 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + i;
-        if (r < nrows) {
-          const float gv = fminf(gs[i], limit);
-          const float uv = fminf(fmaxf(us[i], -limit), limit);
-          h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int rr = rbase + e;
+      if (rr < nrows) {
+        const float gv = fminf(gs[e], limit);
+        const float uv = fminf(fmaxf(us[e], -limit), limit);
+        h_out[static_cast<size_t>(row0 + rr) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
       }
-    } else {
+    }
+  } else {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * wave + jj;
-        const f32x4 os = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
-        const int col = blockIdx.x * 128 + j * 16 + (lane & 15);
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * wave + jj;
+      const f32x4 os = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+      const int col = blockIdx.x * 128 + j * 16 + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + i;
-          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = os[i];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rbase + e;
+        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = os[e];
       }
     }
   }
@@ -380,52 +374,65 @@ __global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(const uint16_t* __r
   }
 }
 
-// Rows per item of the decode kernels (16 * MT) for a given T.
-inline int decode_mt(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
+constexpr int kDecodeRows = 16;
 
-// Decode kernels while the average group holds at most ~16 rows.
-inline bool use_decode(int T, int E, int k) { return static_cast<long>(T) * (k + 1) <= 16L * (E + 1); }
+inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
 
-template <int MT>
-hipError_t launch_decode(const uint16_t* x, const uint8_t* blob, uint64_t eb, int H, int I, const int32_t* row_token,
-                         float limit, float* out_rows, const FfnWs& w, int max_items, hipStream_t s) {
-  dim3 g1(I / 64, max_items), g2(H / 128, max_items);
-  ffn_decode_kernel<MT, true><<<g1, 256, 0, s>>>(x, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h, nullptr);
-  ffn_decode_kernel<MT, false><<<g2, 256, 0, s>>>(w.h, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
-                                                  out_rows);
-  return hipGetLastError();
+// Decode kernels while the average group holds at most ~16 rows (and the K
+// sizes have a compiled decode variant); prefill kernels otherwise.
+inline bool use_decode(int T, int E, int k, int H, int I) {
+  return static_cast<long>(T) * (k + 1) <= 16L * (E + 1) && decode_k_ok(H) && decode_k_ok(I);
 }
 
-inline int ffn_bm(int T, int E, int k) { return use_decode(T, E, k) ? 16 * decode_mt(T) : kPrefillRows; }
+template <bool GATEUP>
+void launch_decode_phase(const uint16_t* act, const int32_t* row_token, const FfnWs& w, const uint8_t* blob,
+                         uint64_t eb, int H, int I, float limit, float* out_rows, int max_items, hipStream_t s) {
+  const int K = GATEUP ? H : I;
+  dim3 grid(GATEUP ? I / 64 : H / 128, max_items);
+  uint16_t* h = GATEUP ? w.h : nullptr;
+  float* o = GATEUP ? nullptr : out_rows;
+  switch (K / 512) {
+    case 1: ffn_decode_kernel<GATEUP, 1><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, h, o); break;
+    case 2: ffn_decode_kernel<GATEUP, 2><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, h, o); break;
+    case 4: ffn_decode_kernel<GATEUP, 4><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, h, o); break;
+    default: ffn_decode_kernel<GATEUP, 8><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, h, o); break;
+  }
+}
+
+inline int ffn_bm(int T, int E, int k, int H, int I) { return use_decode(T, E, k, H, I) ? kDecodeRows : kPrefillRows; }
 
 }  // namespace
 
 size_t ffn_ws_bytes(int T, int E, int H, int I, int k) {
-  (void)H;
-  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k));
+  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I));
   return 256 + align256(sizeof(int4) * static_cast<size_t>(mi)) +
          align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
 }
 
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, hipStream_t s) {
-  const int bm = ffn_bm(T, E, k);
+                      void* ws, int phase, hipStream_t s) {
+  const int bm = ffn_bm(T, E, k, H, I);
   const int max_items = ffn_max_items(T, E, k, bm);
+  const bool dec = use_decode(T, E, k, H, I);
   FfnWs w = ffn_carve(ws, max_items);
-  ffn_plan_kernel<<<1, 256, 0, s>>>(offsets, E, bm, w.items, w.n_items);
-  if (use_decode(T, E, k)) {
-    switch (decode_mt(T)) {
-      case 1: return launch_decode<1>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
-      case 2: return launch_decode<2>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
-      default: return launch_decode<4>(x, blob, expert_bytes, H, I, row_token, limit, out_rows, w, max_items, s);
+  for (int ph = 0; ph < 3; ++ph) {
+    if (phase >= 0 && ph != phase) continue;
+    if (ph == 0) {
+      ffn_plan_kernel<<<1, 256, 0, s>>>(offsets, E, bm, w.items, w.n_items);
+    } else if (dec) {
+      if (ph == 1) launch_decode_phase<true>(x, row_token, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+      else launch_decode_phase<false>(w.h, nullptr, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+    } else if (ph == 1) {
+      dim3 g1(I / 64, max_items);
+      ffn_prefill_kernel<true><<<g1, 256, 0, s>>>(x, row_token, w.items, w.n_items, blob, expert_bytes, H, I, limit,
+                                                  w.h, nullptr);
+    } else {
+      dim3 g2(H / 128, max_items);
+      ffn_prefill_kernel<false><<<g2, 256, 0, s>>>(w.h, nullptr, w.items, w.n_items, blob, expert_bytes, H, I, limit,
+                                                   nullptr, out_rows);
     }
   }
-  dim3 g1(I / 64, max_items), g2(H / 128, max_items);
-  ffn_prefill_kernel<true><<<g1, 256, 0, s>>>(x, row_token, w.items, w.n_items, blob, expert_bytes, H, I, limit, w.h,
-                                              nullptr);
-  ffn_prefill_kernel<false><<<g2, 256, 0, s>>>(w.h, nullptr, w.items, w.n_items, blob, expert_bytes, H, I, limit,
-                                               nullptr, out_rows);
   return hipGetLastError();
 }
 

@@ -112,21 +112,38 @@ size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top
   return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k);
 }
 
-int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k, const int32_t* offsets,
-                   const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes,
-                   void* stream) {
+namespace {
+
+int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k, const int32_t* offsets,
+             const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes, int32_t phase,
+             void* stream) {
   if (T < 0) return MOE_EINVAL;
   const int st = check_experts(experts);
   if (st != MOE_OK) return st;
   if (top_k < 1 || top_k > kMaxTopK) return MOE_ESHAPE;
   if (!(clamp_limit > 0.0f)) return MOE_EINVAL;
+  if (phase < -1 || phase > 2) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !row_token || !out_rows || !ws) return MOE_EINVAL;
   if (!aligned(x, 16) || !aligned(out_rows, 16) || !aligned(ws, 256)) return MOE_EALIGN;
   if (ws_bytes < moe_ffn_workspace_size(T, experts, top_k)) return MOE_EWORKSPACE;
   return hip_status(moe::launch_ffn(x, T, static_cast<const uint8_t*>(experts->base), experts->expert_bytes,
                                     experts->n_experts, experts->hidden, experts->inter, top_k, offsets, row_token,
-                                    clamp_limit, out_rows, ws, as_stream(stream)));
+                                    clamp_limit, out_rows, ws, phase, as_stream(stream)));
+}
+
+}  // namespace
+
+int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k, const int32_t* offsets,
+                   const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return ffn_call(x, T, experts, top_k, offsets, row_token, clamp_limit, out_rows, ws, ws_bytes, -1, stream);
+}
+
+int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
+                         const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
+                         void* ws, size_t ws_bytes, int32_t phase, void* stream) {
+  return ffn_call(x, T, experts, top_k, offsets, row_token, clamp_limit, out_rows, ws, ws_bytes, phase, stream);
 }
 
 int moe_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,

@@ -15,73 +15,114 @@ namespace moe {
 
 namespace {
 
-constexpr int kTokTile = 32;  // tokens per logits block
-constexpr int kHStage = 32;   // h values staged in LDS per step
+constexpr int kExpBlock = 64;   // experts per logits block (one per lane)
+constexpr int kHStage = 16;     // h values per LDS stage
 
 // part[hs][t][e] = sum over h in slice hs of x[t,h] * W[h,e], float64.
-// grid (ceil(T/32), hsplit), 256 threads: thread e owns expert e and keeps the
-// 32 token sums in registers; x is staged in LDS already widened to float64.
+// grid (E/64, ceil(T/TB), hsplit), 256 threads.  Lane l owns expert
+// 64*blockIdx.x + l and keeps TB token sums in registers; wave w sums a
+// quarter of the block's h slice (x staged in LDS already widened to
+// float64); the four wave sums meet in LDS, added in wave order.
+template <int TB>
 __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                            const float* __restrict__ W, int E, int hsplit,
                                                            double* __restrict__ part) {
-  __shared__ double xs[kHStage][kTokTile];
-  const int e = threadIdx.x;
-  const int t0 = blockIdx.x * kTokTile;
+  __shared__ double xs[4][kHStage][TB];
+  __shared__ double red[4][TB][kExpBlock];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kExpBlock + lane;
+  const int t0 = blockIdx.y * TB;
   const int hlen = H / hsplit;
-  const int h0 = blockIdx.y * hlen;
-  double acc[kTokTile];
+  const int hw = hlen / 4;
+  const int h0 = blockIdx.z * hlen + wave * hw;
+  double acc[TB];
 #pragma unroll
-  for (int i = 0; i < kTokTile; ++i) acc[i] = 0.0;
+  for (int i = 0; i < TB; ++i) acc[i] = 0.0;
+  const bool live = e < E;
+  const int ec = live ? e : 0;
 
-  for (int hc = h0; hc < h0 + hlen; hc += kHStage) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < kTokTile * kHStage; i += 256) {
+  for (int hc = h0; hc < h0 + hw; hc += kHStage) {
+    // each wave stages its own x[t0..t0+TB)[hc..hc+16) (one element per lane per pass)
+    for (int i = lane; i < TB * kHStage; i += 64) {
       const int tt = i / kHStage, hh = i % kHStage;
       const int t = t0 + tt;
-      xs[hh][tt] = (t < T) ? static_cast<double>(bf16_bits_to_float(x[static_cast<size_t>(t) * H + hc + hh])) : 0.0;
+      xs[wave][hh][tt] = (t < T) ? static_cast<double>(bf16_bits_to_float(x[static_cast<size_t>(t) * H + hc + hh])) : 0.0;
     }
-    __syncthreads();
-    if (e < E) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll 4
-      for (int hh = 0; hh < kHStage; ++hh) {
-        const double w = static_cast<double>(W[static_cast<size_t>(hc + hh) * E + e]);
+    for (int hh = 0; hh < kHStage; ++hh) {
+      const double w = static_cast<double>(W[static_cast<size_t>(hc + hh) * E + ec]);
 #pragma unroll
-        for (int i = 0; i < kTokTile; ++i) acc[i] = fma(xs[hh][i], w, acc[i]);
-      }
+      for (int i = 0; i < TB; ++i) acc[i] = fma(xs[wave][hh][i], w, acc[i]);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  if (e < E) {
-    for (int i = 0; i < kTokTile; ++i) {
-      const int t = t0 + i;
-      if (t < T) part[(static_cast<size_t>(blockIdx.y) * T + t) * E + e] = acc[i];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  for (int i = wave; i < TB; i += 4) {
+    const int t = t0 + i;
+    if (t < T && live) {
+      const double z = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+      part[(static_cast<size_t>(blockIdx.z) * T + t) * E + e] = z;
     }
   }
 }
 
-// One wave per token: z = sum of the hsplit partial sums (fixed order),
-// s = sqrt(softplus(z)), key = s + bias, k rounds of a wave-wide argmax over
-// (key descending, expert id ascending), then weights from the unbiased s.
+// TPB tokens per block of 256 threads.  Thread e sums the hsplit partial
+// logits of expert e (fixed order) and writes s = sqrt(softplus(z)) and the
+// selection key s + bias to LDS; then wave w runs the top-k of token w: k
+// rounds of a wave-wide argmax over (key descending, expert id ascending),
+// and the weights from the unbiased s.
+template <int TPB>
 __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restrict__ part, int T, int E, int hsplit,
                                                          const float* __restrict__ bias, int k, float scale,
                                                          int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ double s_key[TPB][256];
+  __shared__ double s_sc[TPB][256];
+  const int e = threadIdx.x;
+  const int tb = blockIdx.x * TPB;
+  if (e < E) {
+    const double b = bias ? static_cast<double>(bias[e]) : 0.0;
+#pragma unroll
+    for (int q = 0; q < TPB; ++q) {
+      const int t = tb + q;
+      if (t >= T) break;
+      double z = 0.0;
+      const double* pp = part + static_cast<size_t>(t) * E + e;
+      const size_t stride = static_cast<size_t>(T) * E;
+      int hs = 0;
+      for (; hs + 8 <= hsplit; hs += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pp[(hs + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z += v[u];
+      }
+      for (; hs < hsplit; ++hs) z += pp[hs * stride];
+      const double sc = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));
+      s_sc[q][e] = sc;
+      s_key[q][e] = sc + b;
+    }
+  }
+  __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int q = threadIdx.x >> 6;
+  if (q >= TPB) return;
+  const int t = tb + q;
   if (t >= T) return;
   double key[4], sc[4];
   bool live[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    live[q] = e < E;
-    key[q] = -INFINITY;
-    sc[q] = 0.0;
-    if (live[q]) {
-      double z = 0.0;
-      for (int hs = 0; hs < hsplit; ++hs) z += part[(static_cast<size_t>(hs) * T + t) * E + e];
-      const double sp = fmax(z, 0.0) + log1p(exp(-fabs(z)));
-      sc[q] = sqrt(sp);
-      key[q] = sc[q] + (bias ? static_cast<double>(bias[e]) : 0.0);
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int ee = lane + 64 * u;
+    live[u] = ee < E;
+    key[u] = live[u] ? s_key[q][ee] : -INFINITY;
+    sc[u] = live[u] ? s_sc[q][ee] : 0.0;
   }
   int sel_id[8];
   double sel_s[8];
@@ -93,12 +134,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
     double bk = -INFINITY, bs = 0.0;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (live[q] && (key[q] > bk || (key[q] == bk && e < be))) {
-        bk = key[q];
-        be = e;
-        bs = sc[q];
+    for (int u = 0; u < 4; ++u) {
+      const int ee = lane + 64 * u;
+      if (live[u] && (key[u] > bk || (key[u] == bk && ee < be))) {
+        bk = key[u];
+        be = ee;
+        bs = sc[u];
       }
     }
 #pragma unroll
@@ -115,8 +156,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
     sel_id[j] = be;
     sel_s[j] = bs;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (be == lane + 64 * q) live[q] = false;
+    for (int u = 0; u < 4; ++u)
+      if (be == lane + 64 * u) live[u] = false;
   }
   if (lane == 0) {
     double sum = 0.0;
@@ -148,22 +189,28 @@ __global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restri
 
 }  // namespace
 
-// Number of h slices of the logits: enough blocks to cover the chip, each
-// slice a multiple of the LDS stage and a divisor of H.
+inline int route_tb(int T) { return T <= 256 ? 8 : 32; }
+
+// Number of h slices of the logits: enough blocks to cover the chip while
+// every wave keeps at least one LDS stage of h; always a divisor of H/64.
 int route_hsplit(int T, int H) {
-  const int ntb = (T + kTokTile - 1) / kTokTile;
-  const int max_split = H / kHStage;
+  const int ntb = (T + route_tb(T) - 1) / route_tb(T);
+  const int blocks = ntb * 4;  // E = 256 -> 4 expert blocks
+  const int max_split = H / (4 * kHStage);
   int hs = 1;
-  while (hs * 2 <= max_split && (max_split % (hs * 2)) == 0 && ntb * hs * 2 <= 512) hs *= 2;
+  while (hs * 2 <= max_split && (max_split % (hs * 2)) == 0 && blocks * hs * 2 <= 512) hs *= 2;
   return hs;
 }
 
 hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w, const float* bias, int E, int k,
                                 float scale, int32_t* ids, float* weights, double* part, hipStream_t s) {
   const int hs = route_hsplit(T, H);
-  dim3 g1((T + kTokTile - 1) / kTokTile, hs);
-  route_logits_kernel<<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part);
-  route_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
+  const int tb = route_tb(T);
+  dim3 g1((E + kExpBlock - 1) / kExpBlock, (T + tb - 1) / tb, hs);
+  if (tb == 8) route_logits_kernel<8><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part);
+  else route_logits_kernel<32><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part);
+  if (T <= 256) route_topk_kernel<1><<<T, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
+  else route_topk_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
-FFN_SRC = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc", "ffn.hip")
+CSRC = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -47,12 +47,13 @@ def _parse():
     return p.parse_args()
 
 
-def ffn_source_hash() -> str:
-    with open(FFN_SRC, "rb") as f:
+def source_hash(name: str) -> str:
+    """Short hash of a kernel source file (ffn_decode.hip or ffn_prefill.hip)."""
+    with open(os.path.join(CSRC, name), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload: str, bytes_alg_per_launch: float):
+def read_traffic(workload: str, source: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None when none exists or the kernel source changed since."""
     path = os.path.join(PROFILES, f"ffn_gateup_{workload}_counters.txt")
@@ -64,7 +65,7 @@ def read_traffic(workload: str, bytes_alg_per_launch: float):
             if ":" in line and not line.lstrip().startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("ffn_source_sha256_16") != ffn_source_hash():
+    if kv.get("source") != source or kv.get("source_sha256_16") != source_hash(source):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -183,12 +184,12 @@ def main():
         achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4))
-        traffic = read_traffic(wl.name, gateup_bytes)
+        traffic = read_traffic(wl.name, "ffn_decode.hip")
     else:
         achieved = gateup_flops / (gateup_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4))
-        traffic = read_traffic(wl.name, gateup_bytes)
+        traffic = read_traffic(wl.name, "ffn_prefill.hip")
     roof["traffic"] = traffic
     roof["kernel"] = "ffn gate/up (moe_expert_ffn phase 1)"
     roof["avg_launch_us"] = round(gateup_ms * 1e3, 2)

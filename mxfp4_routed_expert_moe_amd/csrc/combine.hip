@@ -12,40 +12,56 @@ namespace moe {
 
 namespace {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out_rows,
+// All row indices and weights of a token are read first, then all of its
+// row loads are issued together, so a thread waits for one memory round
+// trip, not one per slot.
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ out_rows,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ weights, int T, int H, int k,
                                                       uint16_t* __restrict__ y) {
+  constexpr int kMaxK = 8;
   const int groups = H >> 3;
-  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  const long idx = static_cast<long>(blockIdx.x) * 128 + threadIdx.x;
   const int t = static_cast<int>(idx / groups);
   const int c = static_cast<int>(idx % groups) * 8;
   if (t >= T) return;
+  const int32_t* sr = slot_row + static_cast<size_t>(t) * (k + 1);
+  int rows[kMaxK + 1];
+  float w[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rows[j] = j < k ? sr[j] : -1;
+    w[j] = j < k ? weights[static_cast<size_t>(t) * k + j] : 0.f;
+  }
+  rows[kMaxK] = sr[k];
+  f32x4 v[kMaxK + 1][2];
+#pragma unroll
+  for (int j = 0; j <= kMaxK; ++j) {
+    if (rows[j] >= 0) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(rows[j]) * H + c);
+      v[j][0] = p[0];
+      v[j][1] = p[1];
+    } else {
+      v[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const int32_t* sr = slot_row + static_cast<size_t>(t) * (k + 1);
-  for (int j = 0; j < k; ++j) {
-    const int r = sr[j];
-    if (r < 0) continue;
-    const float w = weights[static_cast<size_t>(t) * k + j];
-    const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(r) * H + c);
-    const f32x4 v0 = p[0], v1 = p[1];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (rows[j] < 0) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[i] = fmaf(w, v0[i], acc[i]);
-      acc[4 + i] = fmaf(w, v1[i], acc[4 + i]);
+      acc[i] = fmaf(w[j], v[j][0][i], acc[i]);
+      acc[4 + i] = fmaf(w[j], v[j][1][i], acc[4 + i]);
     }
   }
-  {
-    const int r = sr[k];
-    const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(r) * H + c);
-    const f32x4 v0 = p[0], v1 = p[1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += v0[i];
-      acc[4 + i] += v1[i];
-    }
+  for (int i = 0; i < 4; ++i) {
+    acc[i] += v[kMaxK][0][i];
+    acc[4 + i] += v[kMaxK][1][i];
   }
   u32x4 o;
 #pragma unroll
@@ -60,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s) {
   const long threads = static_cast<long>(T) * (H / 8);
-  combine_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, s>>>(out_rows, slot_row, weights, T, H, k, y);
+  combine_kernel<<<static_cast<unsigned>((threads + 127) / 128), 128, 0, s>>>(out_rows, slot_row, weights, T, H, k, y);
   return hipGetLastError();
 }
 

@@ -11,6 +11,9 @@
 //  2. per expert (one wave): exclusive scan of its counts over the chunks;
 //  3. per chunk: exclusive scan of the expert totals -> offsets, then every
 //     pair's row = offsets[e] + chunk base + rank, and the shared rows.
+// Small batches (T * k <= 2048) take one single-block kernel with the same
+// result: counts, scan, and each pair's rank among the earlier pairs of its
+// expert counted directly.
 #include "moe_internal.h"
 
 namespace moe {
@@ -116,6 +119,50 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
   }
 }
 
+constexpr int kSmallPairs = 2048;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ row_token,
+                                                              int32_t* __restrict__ slot_row) {
+  __shared__ int sid[kSmallPairs];
+  __shared__ int cnt[1024];
+  __shared__ int tmp[16];
+  const int n = T * k;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E; i += 1024) cnt[i] = 0;
+  for (int i = tid; i < n; i += 1024) {
+    const int e = ids[i];
+    sid[i] = (e >= 0 && e < E) ? e : -1;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024)
+    if (sid[i] >= 0) atomicAdd(&cnt[sid[i]], 1);  // integer counts: order does not matter
+  __syncthreads();
+  const int n_routed = block_excl_scan_1024(cnt, E, tmp);
+  for (int i = tid; i < E; i += 1024) offsets[i] = cnt[i];
+  if (tid == 0) {
+    offsets[E] = n_routed;
+    offsets[E + 1] = n_routed + T;
+  }
+  for (int i = tid; i < n; i += 1024) {
+    const int e = sid[i];
+    const int t = i / k, j = i - t * k;
+    int32_t row = -1;
+    if (e >= 0) {
+      int r = 0;
+      for (int q = 0; q < i; ++q) r += (sid[q] == e) ? 1 : 0;
+      row = cnt[e] + r;
+      row_token[row] = t;
+    }
+    slot_row[static_cast<size_t>(t) * (k + 1) + j] = row;
+  }
+  for (int t = tid; t < T; t += 1024) {
+    row_token[n_routed + t] = t;
+    slot_row[static_cast<size_t>(t) * (k + 1) + k] = n_routed + t;
+  }
+}
+
 }  // namespace
 
 size_t dispatch_ws_bytes(int T, int E, int k) {
@@ -126,6 +173,10 @@ size_t dispatch_ws_bytes(int T, int E, int k) {
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t s) {
+  if (T * k <= kSmallPairs) {
+    dispatch_small_kernel<<<1, 1024, 0, s>>>(ids, T, E, k, offsets, row_token, slot_row);
+    return hipGetLastError();
+  }
   const int nch = (T + kChunk - 1) / kChunk;
   DispatchWs w = carve(ws, T, E, k);
   dispatch_rank_kernel<<<nch, 256, 0, s>>>(ids, T, E, k, nch, w);

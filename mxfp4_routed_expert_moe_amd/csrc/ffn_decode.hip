@@ -1,0 +1,186 @@
+// Expert FFN, decode family (few rows per expert; HBM bound).  Computes, for
+// the rows of one item (at most 16 rows of one expert),
+//   phase 1: h = bf16( silu(min(W_gate x, L)) * clamp(W_up x, -L, L) )
+//   phase 2: out = W_down h
+// ("Model techniques map -- DeepSeek-V4-Flash", row "SwiGLU feed-forward";
+// MXFP4 weights as in "ElytronAI / DeepSeek-v4-Flash", Sizes), streaming the
+// expert's tiled MXFP4 bytes once from HBM into bf16 MFMA B fragments via the
+// hardware scaled FP4 convert.
+#include "ffn_internal.h"
+
+namespace moe {
+
+namespace {
+
+// grid (n blocks, max items), 256 threads, items of at most 16 rows.
+// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles), K = H, A = x
+// rows via row_token, output h.  Otherwise 128 output columns (8 down
+// n-tiles), K = I, A = h rows, output float32 rows.  Wave w owns k tiles
+// [w*KTW, (w+1)*KTW) of all 8 n-tiles.  The k loop is fully unrolled over a
+// ring of three register buffers, so two k tiles (8 KB per wave) of weight
+// loads stay in flight while one is consumed; the activation loads of a tile
+// are issued one tile ahead and before the weight loads two tiles ahead, so
+// the in-order load counter never makes a tile wait for a later one.
+template <bool GATEUP, int KTW>
+__global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
+                                                            const int32_t* __restrict__ row_token,
+                                                            const int4* __restrict__ items,
+                                                            const int32_t* __restrict__ n_items,
+                                                            const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                            int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                            float* __restrict__ out_rows) {
+  constexpr int KT = 4 * KTW;        // k tiles of the whole K axis
+  constexpr int NSW = KTW >= 4 ? KTW / 4 : 1;  // scale words per n-tile per wave
+  const int item = blockIdx.y;
+  if (item >= *n_items) return;
+  const int4 it = items[item];
+  const int g = it.x, row0 = it.y, nrows = it.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kt0 = wave * KTW;
+  const ExpertPlanes pl = expert_planes(H, I);
+  const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+  constexpr uint64_t kTileStride = static_cast<uint64_t>(KT) * 1024;  // bytes between n-tiles
+  constexpr uint64_t kScStride = static_cast<uint64_t>(KT / 4) * 256;
+
+  const uint8_t* nb0;
+  const uint8_t* nb1;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  if (GATEUP) {
+    nb0 = eb + pl.gate_nib + blockIdx.x * 4 * kTileStride;
+    nb1 = eb + pl.up_nib + blockIdx.x * 4 * kTileStride;
+    sb0 = eb + pl.gate_sc + blockIdx.x * 4 * kScStride;
+    sb1 = eb + pl.up_sc + blockIdx.x * 4 * kScStride;
+  } else {
+    nb0 = eb + pl.down_nib + blockIdx.x * 8 * kTileStride;
+    nb1 = nb0 + 4 * kTileStride;
+    sb0 = eb + pl.down_sc + blockIdx.x * 8 * kScStride;
+    sb1 = sb0 + 4 * kScStride;
+  }
+  nb0 += static_cast<uint64_t>(kt0) * 1024 + lane * 16;
+  nb1 += static_cast<uint64_t>(kt0) * 1024 + lane * 16;
+  sb0 += static_cast<uint64_t>(kt0 >> 2) * 256 + lane * 4;
+  sb1 += static_cast<uint64_t>(kt0 >> 2) * 256 + lane * 4;
+
+  // Padded lanes (rows >= nrows) re-read the item's last row; their results
+  // are never stored.
+  const int r = lane & 15;
+  const int p = row0 + min(r, nrows - 1);
+  const uint16_t* arow = (GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I) +
+                         32 * (lane >> 4) + kt0 * 128;
+
+  uint32_t sw[NSW][8];
+#pragma unroll
+  for (int d = 0; d < NSW; ++d)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sw[d][j] = *reinterpret_cast<const uint32_t*>((j < 4 ? sb0 : sb1) + (j & 3) * kScStride + d * 256);
+
+  u32x4 bq[3][8];
+  u32x4 a[2][4];
+  auto load_b = [&](int buf, int i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[buf][j] = ld16((j < 4 ? nb0 : nb1) + (j & 3) * kTileStride + i * 1024);
+  };
+  auto load_a = [&](int buf, int i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[buf][q] = ld16(arow + i * 128 + 8 * q);
+  };
+
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0, 0);
+  load_b(0, 0);
+  if (KTW > 1) {
+    load_a(1, 1);
+    load_b(1, 1);
+  }
+  // sched_barrier(0) keeps the compiler from sinking prefetches below the
+  // MFMAs of the current tile (which would leave one tile in flight).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < KTW; ++i) {
+    if (i + 2 < KTW) load_b((i + 2) % 3, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kt = kt0 + i;
+    const int sh = 8 * (kt & 3);
+    const int d = KTW >= 4 ? (i >> 2) : 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sc = e8m0_to_float((sw[d][j] >> sh) & 255u);
+        acc[j] = mfma16x16x32(av, dequant8(bq[i % 3][j][s], sc), acc[j]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < KTW) load_a(i & 1, i + 2);
+  }
+
+  // Split-K partial sums meet in LDS; summed in wave order 0,1,2,3.
+  __shared__ f32x4 red[4][8][64];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  const int rbase = 4 * (lane >> 4);
+  if (GATEUP) {
+    const int jg = wave, ju = 4 + wave;
+    const f32x4 gs = ((red[0][jg][lane] + red[1][jg][lane]) + red[2][jg][lane]) + red[3][jg][lane];
+    const f32x4 us = ((red[0][ju][lane] + red[1][ju][lane]) + red[2][ju][lane]) + red[3][ju][lane];
+    const int col = blockIdx.x * 64 + wave * 16 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rr = rbase + e;
+      if (rr < nrows) {
+        const float gv = fminf(gs[e], limit);
+        const float uv = fminf(fmaxf(us[e], -limit), limit);
+        h_out[static_cast<size_t>(row0 + rr) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * wave + jj;
+      const f32x4 os = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+      const int col = blockIdx.x * 128 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rbase + e;
+        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = os[e];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
+                       const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
+                       hipStream_t s) {
+  const int K = gateup ? H : I;
+  dim3 grid(gateup ? I / 64 : H / 128, max_items);
+#define MOE_DECODE_LAUNCH(G, KTW)                                                                              \
+  ffn_decode_kernel<G, KTW><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, \
+                                                 G ? w.h : nullptr, G ? nullptr : out_rows)
+  if (gateup) {
+    switch (K / 512) {
+      case 1: MOE_DECODE_LAUNCH(true, 1); break;
+      case 2: MOE_DECODE_LAUNCH(true, 2); break;
+      case 4: MOE_DECODE_LAUNCH(true, 4); break;
+      default: MOE_DECODE_LAUNCH(true, 8); break;
+    }
+  } else {
+    switch (K / 512) {
+      case 1: MOE_DECODE_LAUNCH(false, 1); break;
+      case 2: MOE_DECODE_LAUNCH(false, 2); break;
+      case 4: MOE_DECODE_LAUNCH(false, 4); break;
+      default: MOE_DECODE_LAUNCH(false, 8); break;
+    }
+  }
+#undef MOE_DECODE_LAUNCH
+}
+
+}  // namespace moe

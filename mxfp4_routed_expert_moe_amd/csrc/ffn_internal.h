@@ -1,0 +1,31 @@
+// Internal interface between the expert-FFN driver (ffn.hip) and its two
+// kernel families (ffn_decode.hip, ffn_prefill.hip).
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+// Device-side work list and the h buffer, carved from the FFN workspace.
+struct FfnWs {
+  int32_t* n_items;  // [1]
+  int4* items;       // [max_items] (group, first row, row count, 0)
+  uint16_t* h;       // [rows, I] bf16
+};
+
+constexpr int kDecodeRows = 16;    // rows per decode item
+constexpr int kPrefillRows = 128;  // rows per prefill item
+
+// K sizes with a compiled decode variant.
+inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
+
+// Phase 1 (gateup = true: x rows -> h) or phase 2 (h rows -> out_rows) over
+// the work list; grid (column blocks, max_items), surplus blocks return.
+void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
+                       const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
+                       hipStream_t s);
+void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
+                        const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
+                        hipStream_t s);
+
+}  // namespace moe

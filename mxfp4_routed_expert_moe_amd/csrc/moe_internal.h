@@ -56,6 +56,8 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -117,6 +119,26 @@ __device__ inline int block_excl_scan_256(int* a, int n, int* tmp) {
     if (idx < n) a[idx] = run;
     run += v[i];
   }
+  __syncthreads();
+  return total;
+}
+
+// Exclusive scan of n <= 1024 ints in LDS buffer `a` (in place) by a
+// 1024-thread block, one element per thread; returns the total to every
+// thread.  `tmp` needs 16 ints.
+__device__ inline int block_excl_scan_1024(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x;
+  const int v = tid < n ? a[tid] : 0;
+  const int incl = wave_incl_scan(v);
+  const int wave = tid >> 6;
+  if ((tid & 63) == 63) tmp[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < 16; ++w) {
+    base += (w < wave) ? tmp[w] : 0;
+    total += tmp[w];
+  }
+  if (tid < n) a[tid] = base + incl - v;
   __syncthreads();
   return total;
 }

@@ -16,58 +16,69 @@ namespace moe {
 namespace {
 
 constexpr int kExpBlock = 64;   // experts per logits block (one per lane)
-constexpr int kHStage = 16;     // h values per LDS stage
 
 // part[hs][t][e] = sum over h in slice hs of x[t,h] * W[h,e], float64.
 // grid (E/64, ceil(T/TB), hsplit), 256 threads.  Lane l owns expert
 // 64*blockIdx.x + l and keeps TB token sums in registers; wave w sums a
-// quarter of the block's h slice (x staged in LDS already widened to
-// float64); the four wave sums meet in LDS, added in wave order.
-template <int TB>
+// quarter of the block's h slice in chunks of HC: for each chunk it first
+// issues every load (HC router weights per lane into registers, TB x values
+// per lane into LDS widened to float64), then runs the HC x TB fused
+// multiply-adds, so a chunk costs one memory round trip.  The four wave sums
+// meet in LDS (reusing the x buffer), added in wave order.
+template <int TB, int HC>
 __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __restrict__ x, int T, int H,
                                                            const float* __restrict__ W, int E, int hsplit,
                                                            double* __restrict__ part) {
-  __shared__ double xs[4][kHStage][TB];
-  __shared__ double red[4][TB][kExpBlock];
+  constexpr int kBuf = (HC > 64 ? HC : 64) * TB;
+  __shared__ double buf[4][kBuf];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * kExpBlock + lane;
   const int t0 = blockIdx.y * TB;
-  const int hlen = H / hsplit;
-  const int hw = hlen / 4;
-  const int h0 = blockIdx.z * hlen + wave * hw;
+  const int hw = H / hsplit / 4;
+  const int h0 = blockIdx.z * (H / hsplit) + wave * hw;
+  const bool live = e < E;
+  const int ec = live ? e : 0;
+  double* xs = buf[wave];  // [HC][TB]
   double acc[TB];
 #pragma unroll
   for (int i = 0; i < TB; ++i) acc[i] = 0.0;
-  const bool live = e < E;
-  const int ec = live ? e : 0;
 
-  for (int hc = h0; hc < h0 + hw; hc += kHStage) {
-    // each wave stages its own x[t0..t0+TB)[hc..hc+16) (one element per lane per pass)
-    for (int i = lane; i < TB * kHStage; i += 64) {
-      const int tt = i / kHStage, hh = i % kHStage;
-      const int t = t0 + tt;
-      xs[wave][hh][tt] = (t < T) ? static_cast<double>(bf16_bits_to_float(x[static_cast<size_t>(t) * H + hc + hh])) : 0.0;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll 4
-    for (int hh = 0; hh < kHStage; ++hh) {
-      const double w = static_cast<double>(W[static_cast<size_t>(hc + hh) * E + ec]);
+  for (int hc = h0; hc < h0 + hw; hc += HC) {
+    float wv[HC];
 #pragma unroll
-      for (int i = 0; i < TB; ++i) acc[i] = fma(xs[wave][hh][i], w, acc[i]);
+    for (int hh = 0; hh < HC; ++hh) wv[hh] = W[static_cast<size_t>(hc + hh) * E + ec];
+    uint16_t xv[TB];
+    const bool xl = lane < HC;
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      xv[t] = (xl && t0 + t < T) ? x[static_cast<size_t>(t0 + t) * H + hc + lane] : static_cast<uint16_t>(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (xl) {
+#pragma unroll
+      for (int t = 0; t < TB; ++t) xs[lane * TB + t] = static_cast<double>(bf16_bits_to_float(xv[t]));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+      const double w = static_cast<double>(wv[hh]);
+#pragma unroll
+      for (int i = 0; i < TB; ++i) acc[i] = fma(xs[hh * TB + i], w, acc[i]);
+    }
   }
+  __syncthreads();
+  double* red = &buf[0][0];  // [4][TB][64]
 #pragma unroll
-  for (int i = 0; i < TB; ++i) red[wave][i][lane] = acc[i];
+  for (int i = 0; i < TB; ++i) red[(wave * TB + i) * 64 + lane] = acc[i];
   __syncthreads();
   for (int i = wave; i < TB; i += 4) {
     const int t = t0 + i;
     if (t < T && live) {
-      const double z = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+      const double z = ((red[(0 * TB + i) * 64 + lane] + red[(1 * TB + i) * 64 + lane]) +
+                        red[(2 * TB + i) * 64 + lane]) + red[(3 * TB + i) * 64 + lane];
       part[(static_cast<size_t>(blockIdx.z) * T + t) * E + e] = z;
     }
   }
@@ -191,14 +202,19 @@ __global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restri
 
 inline int route_tb(int T) { return T <= 256 ? 8 : 32; }
 
-// Number of h slices of the logits: enough blocks to cover the chip while
-// every wave keeps at least one LDS stage of h; always a divisor of H/64.
+// Number of h slices: enough blocks to cover the chip, with every wave's h
+// range (H / hsplit / 4) either 16, 32 or a multiple of 64.
 int route_hsplit(int T, int H) {
   const int ntb = (T + route_tb(T) - 1) / route_tb(T);
   const int blocks = ntb * 4;  // E = 256 -> 4 expert blocks
-  const int max_split = H / (4 * kHStage);
   int hs = 1;
-  while (hs * 2 <= max_split && (max_split % (hs * 2)) == 0 && blocks * hs * 2 <= 512) hs *= 2;
+  for (;;) {
+    const int n = hs * 2;
+    if ((H / 4) % n != 0 || blocks * n > 512) break;
+    const int hw = H / 4 / n;
+    if (!(hw == 16 || hw == 32 || hw % 64 == 0)) break;
+    hs = n;
+  }
   return hs;
 }
 
@@ -206,9 +222,17 @@ hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w,
                                 float scale, int32_t* ids, float* weights, double* part, hipStream_t s) {
   const int hs = route_hsplit(T, H);
   const int tb = route_tb(T);
+  const int hw = H / hs / 4;
   dim3 g1((E + kExpBlock - 1) / kExpBlock, (T + tb - 1) / tb, hs);
-  if (tb == 8) route_logits_kernel<8><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part);
-  else route_logits_kernel<32><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part);
+#define MOE_LOGITS(TB_, HC_) route_logits_kernel<TB_, HC_><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part)
+  if (tb == 8) {
+    if (hw == 16) MOE_LOGITS(8, 16);
+    else if (hw == 32) MOE_LOGITS(8, 32);
+    else MOE_LOGITS(8, 64);
+  } else {
+    MOE_LOGITS(32, 16);  // compute-bound regime: a short chunk keeps registers for the 32 token sums
+  }
+#undef MOE_LOGITS
   if (T <= 256) route_topk_kernel<1><<<T, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   else route_topk_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   return hipGetLastError();

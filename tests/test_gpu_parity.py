@@ -163,6 +163,36 @@ def test_edge_cases_empty_and_dropped_ids():
     LC.assert_output_close(O.bf16_bits_to_f64(LC.host(layer.y).view(np.uint16)), y, "dropped ids")
 
 
+@pytest.mark.parametrize("T", [50, 400])   # single-block dispatch (T*6 <= 2048) and the chunked path
+def test_dispatch_duplicates_and_invalid_ids(T):
+    E = 40
+    g = np.random.default_rng(T)
+    ids = g.integers(0, E, size=(T, 6)).astype(np.int32)      # repeats inside a token are allowed
+    ids[g.integers(0, T, 7), g.integers(0, 6, 7)] = E + 1       # dropped
+    ids[g.integers(0, T, 5), g.integers(0, 6, 5)] = -3          # dropped
+    off, rt, sr = B.dispatch(LC.dev(ids), E)
+    o2, r2, s2 = O.dispatch(ids, E)
+    assert np.array_equal(LC.host(off), o2)
+    assert np.array_equal(LC.host(rt)[: o2[-1]], r2)
+    assert np.array_equal(LC.host(sr), s2)
+
+
+@pytest.mark.parametrize("T", [20, 300])
+def test_ffn_phases_equal_one_call(T):
+    inp = _small_inputs(T, 512, 512, 16, 66)
+    ex = _experts(inp)
+    a = LC.run_gpu_layer(inp, ex)
+    layer = a["layer"]
+    ref = layer.out_rows.clone()
+    layer.out_rows.zero_()
+    xd = LC.dev(inp.x)
+    for ph in (0, 1, 2):
+        layer.expert_ffn_phase(xd, ph)
+    torch.cuda.synchronize()
+    n = int(a["offsets"][-1])
+    assert torch.equal(layer.out_rows[:n], ref[:n])
+
+
 def test_hash_out_of_range_token_gives_dropped_ids():
     E = 16
     table, tok = WL.make_hash(3, 10, E, 6, vocab=50)

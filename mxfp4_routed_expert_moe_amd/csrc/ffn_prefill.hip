@@ -7,152 +7,219 @@ namespace moe {
 
 namespace {
 
-constexpr int kLdsPitch = 136;  // bf16 per LDS row: 128 + 8 of padding (272 bytes)
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-// grid (n blocks, max items), 256 threads = 2 x 2 waves, 128-row items.
-// GATEUP: 64 output columns per block (wave column wn: gate and up n-tiles of
-// output columns 32*wn .. 32*wn+31).  Otherwise 128 output columns per block
-// (wave column wn: 4 down n-tiles).
+// Block barrier for the activation ring.  Unlike __syncthreads() it does not
+// drain the vector-memory counter, so the prefetched tiles stay in flight
+// across it.  No release fence is needed: the only LDS writes are LDS-DMA
+// loads, which each wave has already waited for explicitly (wait_vmcnt), and
+// every LDS read before it has been consumed by an MFMA.  The acquire fence
+// keeps later LDS reads below the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
+constexpr int kAhead = 3;         // tiles in flight ahead of the one being multiplied
+constexpr int kOpsPerTile = 16;   // vector-memory ops per lane per tile: 8 weight loads + 8 LDS-DMA loads
+constexpr int kScaleOps = 8;      // one scale word per n-tile per group of four tiles
+
+// grid (n blocks, max items) of 256 threads = 2 x 2 waves, one wave per SIMD
+// (the full register file: 4 x 8 MFMA 16x16x32 accumulators per wave plus a
+// four-deep ring of weight fragments).  Items hold up to 128 rows of one
+// expert.  A block covers 128 rows x 256 weight columns: GATEUP -> 128 output
+// columns (wave column wn: gate and up n-tiles of output columns 64*wn ..
+// 64*wn+63), otherwise 256 down columns (wave column wn: 8 n-tiles).
+//
+// Activation tiles (128 rows x 128 k, 32 KB) go from global memory straight
+// into LDS with the LDS-DMA load (global_load_lds_dwordx4) into a ring of
+// four stages.  Row r of a tile occupies 256 bytes; its 16-byte chunk c sits
+// at slot c ^ (r & 15), so an MFMA fragment read (16 rows, same chunk) hits 16
+// distinct bank groups.  The DMA puts each wave's 64 lanes in 1 KB of
+// contiguous LDS, so the swizzle is applied on the global side: the lane that
+// lands in slot s of row r loads chunk s ^ (r & 15).
+//
+// Pipeline: tile kt+3 (weights into registers, then activations into LDS) is
+// issued while tile kt is multiplied; before tile kt the wave waits until at
+// most the ops of the later tiles (and one group of scale words) are still
+// outstanding, then the block barrier publishes every wave's DMA writes and
+// frees the stage that tile kt+3 reuses.
+//
+// Block order is remapped so the n blocks of one item run on the same XCD:
+// blocks go to the 8 XCDs round robin, and block b takes logical work
+// b % 8 * ceil(total / 8) + b / 8, so consecutive logical blocks (the column
+// blocks of one item, then the next item of the same expert) share an L2.
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
                                                              const int32_t* __restrict__ n_items,
                                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes,
                                                              int H, int I, float limit, uint16_t* __restrict__ h_out,
                                                              float* __restrict__ out_rows) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kPrefillRows * kLdsPitch];
-  const int item = blockIdx.y;
-  if (item >= *n_items) return;
-  const int4 it = items[item];
+  __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
+  const int nbc = gridDim.x;
+  const int total = *n_items * nbc;
+  const int b = blockIdx.x + blockIdx.y * nbc;
+  const int per = (total + 7) >> 3;
+  if ((b >> 3) >= per) return;
+  const int lam = (b & 7) * per + (b >> 3);
+  if (lam >= total) return;
+  const int4 it = items[lam / nbc];
+  const int nb = lam % nbc;
   const int g = it.x, row0 = it.y, nrows = it.z;
   const int K = GATEUP ? H : I;
-  const int KT = K >> 7;
+  const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const ExpertPlanes pl = expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+  const uint64_t tstride = static_cast<uint64_t>(KT) * 1024;  // bytes between n-tiles
+  const uint64_t sstride = static_cast<uint64_t>(KT >> 2) * 256;
 
-  const uint8_t* nib[4];
-  const uint8_t* scl[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int nt;
-    uint64_t onib, osc;
-    if (GATEUP) {
-      nt = blockIdx.x * 4 + wn * 2 + (j & 1);
-      onib = j < 2 ? pl.gate_nib : pl.up_nib;
-      osc = j < 2 ? pl.gate_sc : pl.up_sc;
-    } else {
-      nt = blockIdx.x * 8 + wn * 4 + j;
-      onib = pl.down_nib;
-      osc = pl.down_sc;
-    }
-    nib[j] = eb + onib + static_cast<uint64_t>(nt) * KT * 1024 + lane * 16;
-    scl[j] = eb + osc + static_cast<uint64_t>(nt) * (KT >> 2) * 256 + lane * 4;
+  const uint8_t* nb0;
+  const uint8_t* nb1;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  if (GATEUP) {
+    const int nt0 = nb * 8 + wn * 4;
+    nb0 = eb + pl.gate_nib + nt0 * tstride;
+    nb1 = eb + pl.up_nib + nt0 * tstride;
+    sb0 = eb + pl.gate_sc + nt0 * sstride;
+    sb1 = eb + pl.up_sc + nt0 * sstride;
+  } else {
+    const int nt0 = nb * 16 + wn * 8;
+    nb0 = eb + pl.down_nib + nt0 * tstride;
+    nb1 = nb0 + 4 * tstride;
+    sb0 = eb + pl.down_sc + nt0 * sstride;
+    sb1 = sb0 + 4 * sstride;
   }
+  nb0 += lane * 16;
+  nb1 += lane * 16;
+  sb0 += lane * 4;
+  sb1 += lane * 4;
 
-  // A loader: 16 threads per row (16 bytes each = one 128-wide k tile row),
-  // rows tid/16 + 16*q.
-  const int lc = tid & 15, lr = tid >> 4;
-  const uint16_t* ldp[8];
+  // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
+  // the item reload its last row (never stored).
+  const char* asrc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const int r = lr + 16 * q;
-    ldp[q] = nullptr;
-    if (r < nrows) {
-      const int p = row0 + r;
-      ldp[q] = (GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I) + lc * 8;
-    }
+    const int r = 16 * q + 4 * wave + (lane >> 4);
+    const int p = row0 + min(r, nrows - 1);
+    const uint16_t* rowp = GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I;
+    asrc[q] = reinterpret_cast<const char*>(rowp) + 16 * ((lane & 15) ^ (r & 15));
   }
 
-  f32x4 acc[4][4];
+  u32x4 bq[kStages][8];
+  uint32_t sw[8], swn[8];
+  auto issue_tile = [&](int stage, int kt) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bq[stage][j] = ld16((j < 4 ? nb0 : nb1) + (j & 3) * tstride + kt * 1024);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][(16 * q + 4 * wave) * 128], 16, 0, 0);
+  };
+  auto issue_scales = [&](uint32_t* dst, int grp) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      dst[j] = *reinterpret_cast<const uint32_t*>((j < 4 ? sb0 : sb1) + (j & 3) * sstride + grp * 256);
+  };
+
+  f32x4 acc[4][8];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 areg[8];
-  u32x4 bq[4], bn[4];
-  uint32_t sw[4];
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) areg[q] = ldp[q] ? ld16(ldp[q] + kt * 128) : u32x4{0u, 0u, 0u, 0u};
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      *reinterpret_cast<u32x4*>(&As[buf][(lr + 16 * q) * kLdsPitch + lc * 8]) = areg[q];
-  };
+  issue_scales(sw, 0);
+  issue_tile(0, 0);
+  issue_tile(1, 1);
+  issue_tile(2, 2);
+  __builtin_amdgcn_sched_barrier(0);
 
-  load_a(0);
+  const int arow = wm * 64 + (lane & 15);
+  const int g4 = lane >> 4;
+  const int groups = KT >> 2;
+  for (int u = 0; u < groups; ++u) {
+    const bool last = u + 1 == groups;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bq[j] = ld16(nib[j]);
-  store_a(0);
-  __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+      const int kt = 4 * u + i;
+      // Tile kt is complete once at most the ops issued after it are pending:
+      // tiles kt+1, kt+2, plus the scale words issued at the start of this
+      // group when that came after tile kt (i = 1, 2).  The last group drains.
+      if (last) {
+        wait_vmcnt<0>();
+      } else if (i == 1 || i == 2) {
+        wait_vmcnt<2 * kOpsPerTile + kScaleOps>();
+      } else {
+        wait_vmcnt<2 * kOpsPerTile>();
+      }
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0 && !last) issue_scales(swn, u + 1);
+      if (kt + kAhead < KT) issue_tile((i + kAhead) % kStages, kt + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
+      float scf[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bn[j] = ld16(nib[j] + static_cast<size_t>(kt + 1) * 1024);
-    }
-    if ((kt & 3) == 0) {
+      for (int j = 0; j < 8; ++j) scf[j] = e8m0_to_float((sw[j] >> (8 * i)) & 255u);
+      const uint16_t* abuf = As[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sw[j] = *reinterpret_cast<const uint32_t*>(scl[j] + static_cast<size_t>(kt >> 2) * 256);
-    }
-    float scf[4];
-    const int sh = 8 * (kt & 3);
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 a[4];
+        const int slot = ((4 * g4 + s) ^ (lane & 15)) * 8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) scf[j] = e8m0_to_float((sw[j] >> sh) & 255u);
-    const uint16_t* abase = &As[kt & 1][(wm * 64 + (lane & 15)) * kLdsPitch + 32 * (lane >> 4)];
+        for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 b[4];
+        for (int j = 0; j < 8; ++j) {
+          const bf16x8 bv = dequant8(bq[i][j][s], scf[j]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = dequant8(bq[j][s], scf[j]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mt * 16 * kLdsPitch + 8 * s);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mt][j] = mfma16x16x32(a, b[j], acc[mt][j]);
+          for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
+        }
       }
     }
-    if (more) {
-      store_a((kt + 1) & 1);
+    if (!last) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bq[j] = bn[j];
+      for (int j = 0; j < 8; ++j) sw[j] = swn[j];
     }
-    __syncthreads();
   }
 
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const int rbase = wm * 64 + mt * 16 + 4 * (lane >> 4);
+    const int rbase = wm * 64 + mt * 16 + 4 * g4;
     if (GATEUP) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = blockIdx.x * 64 + wn * 32 + j * 16 + (lane & 15);
+      for (int j = 0; j < 4; ++j) {
+        const int col = nb * 128 + wn * 64 + j * 16 + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + i;
+        for (int e = 0; e < 4; ++e) {
+          const int r = rbase + e;
           if (r < nrows) {
-            const float gv = fminf(acc[mt][j][i], limit);
-            const float uv = fminf(fmaxf(acc[mt][j + 2][i], -limit), limit);
+            const float gv = fminf(acc[mt][j][e], limit);
+            const float uv = fminf(fmaxf(acc[mt][j + 4][e], -limit), limit);
             h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
           }
         }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = blockIdx.x * 128 + wn * 64 + j * 16 + (lane & 15);
+      for (int j = 0; j < 8; ++j) {
+        const int col = nb * 256 + wn * 128 + j * 16 + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rbase + i;
-          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = acc[mt][j][i];
+        for (int e = 0; e < 4; ++e) {
+          const int r = rbase + e;
+          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = acc[mt][j][e];
         }
       }
     }
@@ -165,11 +232,11 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
                         hipStream_t s) {
   if (gateup) {
-    dim3 g1(I / 64, max_items);
+    dim3 g1(I / 128, max_items);
     ffn_prefill_kernel<true><<<g1, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h,
                                                 nullptr);
   } else {
-    dim3 g2(H / 128, max_items);
+    dim3 g2(H / 256, max_items);
     ffn_prefill_kernel<false><<<g2, 256, 0, s>>>(act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
                                                  out_rows);
   }

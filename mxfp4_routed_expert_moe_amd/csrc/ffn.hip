@@ -94,12 +94,13 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
   for (int ph = 0; ph < 3; ++ph) {
     if (phase >= 0 && ph != phase) continue;
     if (ph == 0) {
-      ffn_plan_kernel<<<1, 256, 0, s>>>(offsets, E, bm, w.items, w.n_items);
+      // the decode family reads the offsets directly: no work list to build
+      if (!dec) ffn_plan_kernel<<<1, 256, 0, s>>>(offsets, E, bm, w.items, w.n_items);
     } else {
       const bool gateup = ph == 1;
       const uint16_t* act = gateup ? x : w.h;
       const int32_t* rt = gateup ? row_token : nullptr;
-      if (dec) launch_ffn_decode(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+      if (dec) launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, s);
       else launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
     }
   }

@@ -12,29 +12,16 @@ namespace moe {
 
 namespace {
 
-// grid (n blocks, max items), 256 threads, items of at most 16 rows.
-// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles), K = H, A = x
-// rows via row_token, output h.  Otherwise 128 output columns (8 down
-// n-tiles), K = I, A = h rows, output float32 rows.  Wave w owns k tiles
-// [w*KTW, (w+1)*KTW) of all 8 n-tiles.  The k loop is fully unrolled over a
-// ring of three register buffers, so two k tiles (8 KB per wave) of weight
-// loads stay in flight while one is consumed; the activation loads of a tile
-// are issued one tile ahead and before the weight loads two tiles ahead, so
-// the in-order load counter never makes a tile wait for a later one.
+// One chunk of at most 16 rows [row0, row0 + nrows) of group g.  red: the
+// block's LDS for the split-K reduction.
 template <bool GATEUP, int KTW>
-__global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
-                                                            const int32_t* __restrict__ row_token,
-                                                            const int4* __restrict__ items,
-                                                            const int32_t* __restrict__ n_items,
-                                                            const uint8_t* __restrict__ blob, uint64_t expert_bytes,
-                                                            int H, int I, float limit, uint16_t* __restrict__ h_out,
-                                                            float* __restrict__ out_rows) {
+__device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
+                                             int g, int row0, int nrows, const uint8_t* __restrict__ blob,
+                                             uint64_t expert_bytes, int H, int I, float limit,
+                                             uint16_t* __restrict__ h_out, float* __restrict__ out_rows,
+                                             f32x4 (*red)[8][64]) {
   constexpr int KT = 4 * KTW;        // k tiles of the whole K axis
   constexpr int NSW = KTW >= 4 ? KTW / 4 : 1;  // scale words per n-tile per wave
-  const int item = blockIdx.y;
-  if (item >= *n_items) return;
-  const int4 it = items[item];
-  const int g = it.x, row0 = it.y, nrows = it.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kt0 = wave * KTW;
   const ExpertPlanes pl = expert_planes(H, I);
@@ -121,7 +108,6 @@ __global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __re
   }
 
   // Split-K partial sums meet in LDS; summed in wave order 0,1,2,3.
-  __shared__ f32x4 red[4][8][64];
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
@@ -155,16 +141,64 @@ __global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __re
   }
 }
 
+// grid (n blocks, E + ceil(T / 16)), 256 threads: block row y < E takes the
+// rows of routed expert y (16 at a time; an expert with no rows returns at
+// once), the rest take 16-row chunks of the shared group, so the decode path
+// needs no work list.
+// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles), K = H, A = x
+// rows via row_token, output h.  Otherwise 128 output columns (8 down
+// n-tiles), K = I, A = h rows, output float32 rows.  Wave w owns k tiles
+// [w*KTW, (w+1)*KTW) of all 8 n-tiles.  The k loop is fully unrolled over a
+// ring of three register buffers, so two k tiles (8 KB per wave) of weight
+// loads stay in flight while one is consumed; the activation loads of a tile
+// are issued one tile ahead and before the weight loads two tiles ahead, so
+// the in-order load counter never makes a tile wait for a later one.
+template <bool GATEUP, int KTW>
+__global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
+                                                            const int32_t* __restrict__ row_token,
+                                                            const int32_t* __restrict__ offsets, int E,
+                                                            const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                            int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                            float* __restrict__ out_rows) {
+  // blockIdx.y < E: routed expert y, all of its rows (16 at a time);
+  // otherwise chunk y - E of the shared group (16 rows).
+  int g, first, end;
+  if (static_cast<int>(blockIdx.y) < E) {
+    g = blockIdx.y;
+    first = offsets[g];
+    end = offsets[g + 1];
+  } else {
+    g = E;
+    first = offsets[E] + (blockIdx.y - E) * kDecodeRows;
+    end = min(first + kDecodeRows, offsets[E + 1]);
+  }
+  if (first >= end) return;
+  __shared__ f32x4 red[4][8][64];
+  decode_chunk<GATEUP, KTW>(act, row_token, g, first, min(kDecodeRows, end - first), blob, expert_bytes, H, I,
+                            limit, h_out, out_rows, red);
+  // Experts with more than 16 rows (rare while decoding) take further chunks.
+  for (int row0 = first + kDecodeRows; row0 < end; row0 += kDecodeRows) {
+    __syncthreads();  // the previous chunk is done with red
+    // The weight addresses do not depend on the chunk; this empty asm hides
+    // that from the compiler, which would otherwise hoist dozens of them out
+    // of the loop and spill.
+    const uint8_t* bl = blob;
+    asm volatile("" : "+s"(bl));
+    decode_chunk<GATEUP, KTW>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H, I,
+                              limit, h_out, out_rows, red);
+  }
+}
+
 }  // namespace
 
-void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
-                       const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
-                       hipStream_t s) {
+void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
+                       int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
+                       float* out_rows, hipStream_t s) {
   const int K = gateup ? H : I;
-  dim3 grid(gateup ? I / 64 : H / 128, max_items);
-#define MOE_DECODE_LAUNCH(G, KTW)                                                                              \
-  ffn_decode_kernel<G, KTW><<<grid, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, \
-                                                 G ? w.h : nullptr, G ? nullptr : out_rows)
+  dim3 grid(gateup ? I / 64 : H / 128, E + (T + kDecodeRows - 1) / kDecodeRows);
+#define MOE_DECODE_LAUNCH(G, KTW)                                                                            \
+  ffn_decode_kernel<G, KTW><<<grid, 256, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit,        \
+                                                 G ? h : nullptr, G ? nullptr : out_rows)
   if (gateup) {
     switch (K / 512) {
       case 1: MOE_DECODE_LAUNCH(true, 1); break;

@@ -12,6 +12,8 @@ namespace moe {
 
 namespace {
 
+constexpr int kWaves = 4;  // waves per block; they split the K axis
+
 // One chunk of at most 16 rows [row0, row0 + nrows) of group g.  red: the
 // block's LDS for the split-K reduction.
 template <bool GATEUP, int KTW>
@@ -20,8 +22,9 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
                                              uint64_t expert_bytes, int H, int I, float limit,
                                              uint16_t* __restrict__ h_out, float* __restrict__ out_rows,
                                              f32x4 (*red)[8][64]) {
-  constexpr int KT = 4 * KTW;        // k tiles of the whole K axis
+  constexpr int KT = kWaves * KTW;    // k tiles of the whole K axis
   constexpr int NSW = KTW >= 4 ? KTW / 4 : 1;  // scale words per n-tile per wave
+  static_assert(KTW % 4 == 0 || 4 % KTW == 0, "a wave's k tiles tile its scale words");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kt0 = wave * KTW;
   const ExpertPlanes pl = expert_planes(H, I);
@@ -107,30 +110,41 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
     if (i + 2 < KTW) load_a(i & 1, i + 2);
   }
 
-  // Split-K partial sums meet in LDS; summed in wave order 0,1,2,3.
+  // Split-K partial sums meet in LDS; summed in wave order.
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[wave][j][lane] = acc[j];
   __syncthreads();
+  auto wave_sum = [&](int j) {
+    f32x4 v = red[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[w][j][lane];
+    return v;
+  };
   const int rbase = 4 * (lane >> 4);
   if (GATEUP) {
-    const int jg = wave, ju = 4 + wave;
-    const f32x4 gs = ((red[0][jg][lane] + red[1][jg][lane]) + red[2][jg][lane]) + red[3][jg][lane];
-    const f32x4 us = ((red[0][ju][lane] + red[1][ju][lane]) + red[2][ju][lane]) + red[3][ju][lane];
-    const int col = blockIdx.x * 64 + wave * 16 + (lane & 15);
+    constexpr int kPer = 4 / kWaves;  // output n-tiles (gate, up pairs) per wave
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rr = rbase + e;
-      if (rr < nrows) {
-        const float gv = fminf(gs[e], limit);
-        const float uv = fminf(fmaxf(us[e], -limit), limit);
-        h_out[static_cast<size_t>(row0 + rr) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+    for (int jj = 0; jj < kPer; ++jj) {
+      const int jg = wave * kPer + jj;
+      const f32x4 gs = wave_sum(jg);
+      const f32x4 us = wave_sum(4 + jg);
+      const int col = blockIdx.x * 64 + jg * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rbase + e;
+        if (rr < nrows) {
+          const float gv = fminf(gs[e], limit);
+          const float uv = fminf(fmaxf(us[e], -limit), limit);
+          h_out[static_cast<size_t>(row0 + rr) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+        }
       }
     }
   } else {
+    constexpr int kPer = 8 / kWaves;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * wave + jj;
-      const f32x4 os = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+    for (int jj = 0; jj < kPer; ++jj) {
+      const int j = wave * kPer + jj;
+      const f32x4 os = wave_sum(j);
       const int col = blockIdx.x * 128 + j * 16 + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -141,7 +155,7 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
   }
 }
 
-// grid (n blocks, E + ceil(T / 16)), 256 threads: block row y < E takes the
+// grid (n blocks, E + ceil(T / 16)), 64 * kWaves threads: block row y < E takes the
 // rows of routed expert y (16 at a time; an expert with no rows returns at
 // once), the rest take 16-row chunks of the shared group, so the decode path
 // needs no work list.
@@ -154,7 +168,7 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
 // are issued one tile ahead and before the weight loads two tiles ahead, so
 // the in-order load counter never makes a tile wait for a later one.
 template <bool GATEUP, int KTW>
-__global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets, int E,
                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
@@ -173,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void ffn_decode_kernel(const uint16_t* __re
     end = min(first + kDecodeRows, offsets[E + 1]);
   }
   if (first >= end) return;
-  __shared__ f32x4 red[4][8][64];
+  __shared__ f32x4 red[kWaves][8][64];
   decode_chunk<GATEUP, KTW>(act, row_token, g, first, min(kDecodeRows, end - first), blob, expert_bytes, H, I,
                             limit, h_out, out_rows, red);
   // Experts with more than 16 rows (rare while decoding) take further chunks.
@@ -197,21 +211,21 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
   const int K = gateup ? H : I;
   dim3 grid(gateup ? I / 64 : H / 128, E + (T + kDecodeRows - 1) / kDecodeRows);
 #define MOE_DECODE_LAUNCH(G, KTW)                                                                            \
-  ffn_decode_kernel<G, KTW><<<grid, 256, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit,        \
+  ffn_decode_kernel<G, KTW><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit,        \
                                                  G ? h : nullptr, G ? nullptr : out_rows)
   if (gateup) {
-    switch (K / 512) {
-      case 1: MOE_DECODE_LAUNCH(true, 1); break;
+    switch (K / (128 * kWaves)) {
       case 2: MOE_DECODE_LAUNCH(true, 2); break;
       case 4: MOE_DECODE_LAUNCH(true, 4); break;
-      default: MOE_DECODE_LAUNCH(true, 8); break;
+      case 8: MOE_DECODE_LAUNCH(true, 8); break;
+      default: MOE_DECODE_LAUNCH(true, 16); break;
     }
   } else {
-    switch (K / 512) {
-      case 1: MOE_DECODE_LAUNCH(false, 1); break;
+    switch (K / (128 * kWaves)) {
       case 2: MOE_DECODE_LAUNCH(false, 2); break;
       case 4: MOE_DECODE_LAUNCH(false, 4); break;
-      default: MOE_DECODE_LAUNCH(false, 8); break;
+      case 8: MOE_DECODE_LAUNCH(false, 8); break;
+      default: MOE_DECODE_LAUNCH(false, 16); break;
     }
   }
 #undef MOE_DECODE_LAUNCH

@@ -102,7 +102,7 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
       const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float sc = e8m0_to_float((sw[d][j] >> sh) & 255u);
+        const float sc = e8m0_scale_operand((sw[d][j] >> sh) & 255u);
         acc[j] = mfma16x16x32(av, dequant8(bq[i % 3][j][s], sc), acc[j]);
       }
     }
@@ -209,25 +209,26 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
                        int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
                        float* out_rows, hipStream_t s) {
   const int K = gateup ? H : I;
+  const int ktw = K / (128 * kWaves);  // k tiles per wave; decode_k_ok(K) keeps it in {1, 2, 4, 8}
   dim3 grid(gateup ? I / 64 : H / 128, E + (T + kDecodeRows - 1) / kDecodeRows);
 #define MOE_DECODE_LAUNCH(G, KTW)                                                                            \
-  ffn_decode_kernel<G, KTW><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit,        \
-                                                 G ? h : nullptr, G ? nullptr : out_rows)
-  if (gateup) {
-    switch (K / (128 * kWaves)) {
-      case 2: MOE_DECODE_LAUNCH(true, 2); break;
-      case 4: MOE_DECODE_LAUNCH(true, 4); break;
-      case 8: MOE_DECODE_LAUNCH(true, 8); break;
-      default: MOE_DECODE_LAUNCH(true, 16); break;
-    }
-  } else {
-    switch (K / (128 * kWaves)) {
-      case 2: MOE_DECODE_LAUNCH(false, 2); break;
-      case 4: MOE_DECODE_LAUNCH(false, 4); break;
-      case 8: MOE_DECODE_LAUNCH(false, 8); break;
-      default: MOE_DECODE_LAUNCH(false, 16); break;
-    }
+  ffn_decode_kernel<G, KTW><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit, \
+                                                         G ? h : nullptr, G ? nullptr : out_rows)
+#define MOE_DECODE_SWITCH(G)                     \
+  switch (ktw) {                                 \
+    case 1: MOE_DECODE_LAUNCH(G, 1); break;      \
+    case 2: MOE_DECODE_LAUNCH(G, 2); break;      \
+    case 4: MOE_DECODE_LAUNCH(G, 4); break;      \
+    case 8: MOE_DECODE_LAUNCH(G, 8); break;      \
+    default: break; /* excluded by decode_k_ok */ \
   }
+  if (ktw * 128 * kWaves != K) return;  // never taken: decode_k_ok(K) holds for the decode path
+  if (gateup) {
+    MOE_DECODE_SWITCH(true)
+  } else {
+    MOE_DECODE_SWITCH(false)
+  }
+#undef MOE_DECODE_SWITCH
 #undef MOE_DECODE_LAUNCH
 }
 

@@ -16,7 +16,8 @@ struct FfnWs {
 constexpr int kDecodeRows = 16;    // rows per decode item
 constexpr int kPrefillRows = 128;  // rows per prefill item
 
-// K sizes with a compiled decode variant.
+// K sizes with a compiled decode variant (k tiles per wave: K / 512 with
+// four K-splitting waves, one of 1, 2, 4, 8).
 inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
 
 // Phase 1 (gateup = true: x rows -> h) or phase 2 (h rows -> out_rows).

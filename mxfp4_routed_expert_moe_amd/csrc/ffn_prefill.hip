@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
 
       float scf[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) scf[j] = e8m0_to_float((sw[j] >> (8 * i)) & 255u);
+      for (int j = 0; j < 8; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
       const uint16_t* abuf = As[i];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {

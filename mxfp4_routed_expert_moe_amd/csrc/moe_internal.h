@@ -30,13 +30,16 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 }
 
 // ---------------------------------------------------------------- MXFP4
-// E8M0 scale byte -> float32 2^(e-127): e = 0 is the subnormal 2^-127 and
-// e = 255 is NaN (OCP microscaling E8M0).
-__device__ __forceinline__ float e8m0_to_float(uint32_t e) {
-  uint32_t bits = e << 23;
-  bits = (e == 0u) ? 0x00400000u : bits;
-  bits = (e == 255u) ? 0x7fc00000u : bits;
-  return __uint_as_float(bits);
+// Scale operand of the scaled FP4 convert for E8M0 byte e (value 2^(e-127),
+// e = 255 NaN).  The convert reads only the exponent field of its float
+// scale operand, as an E8M0 value: e << 23 places the byte there, and the
+// convert then scales exactly for every e, including e = 0 (2^-127) and
+// e = 255 (NaN) -- checked on gfx950 for all 256 bytes and all 16 codes.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
+
+// Byte i (0..3) of a word of four E8M0 scales, as a convert scale operand.
+__device__ __forceinline__ float e8m0_scale_operand_of(uint32_t word, int i) {
+  return __uint_as_float(((word >> (8 * i)) & 255u) << 23);
 }
 
 // Eight E2M1 codes (one 32-bit word, low nibble first) times one scale ->

@@ -65,6 +65,17 @@ def test_layer_small_shapes(T, H, I, E, routing, bias):
     LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
 
 
+@pytest.mark.parametrize("T", [6, 300])   # decode and prefill kernels
+def test_wide_scale_range(T):
+    # E8M0 scales over 2^-27 .. 2^13: exercises the scale operand of the
+    # convert across exponents and saturates the clamp on most rows
+    H, I, E = 512, 512, 16
+    inp = _small_inputs(T, H, I, E, 4242)
+    inp.experts = WL.make_experts(4242, E + 1, H, I, scale_lo=100, scale_hi=140)
+    r = LC.full_check(inp, _experts(inp))
+    assert r["ambiguous"] == 0
+
+
 def test_determinism_bitwise():
     inp = _small_inputs(300, 512, 512, 16, 77)
     ex = _experts(inp)

@@ -30,15 +30,21 @@ __device__ __forceinline__ void lds_barrier() {
 
 constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
 constexpr int kAhead = 3;         // tiles in flight ahead of the one being multiplied
-constexpr int kOpsPerTile = 16;   // vector-memory ops per lane per tile: 8 weight loads + 8 LDS-DMA loads
-constexpr int kScaleOps = 8;      // one scale word per n-tile per group of four tiles
+constexpr int kWavesM = 2, kWavesN = 4;        // 8 waves: 2 along the rows x 4 along the columns
+constexpr int kThreads = 64 * kWavesM * kWavesN;
+constexpr int kNT = 16 / kWavesN;                // weight n-tiles per wave
+constexpr int kDmaOps = 2048 / kThreads;         // 16-byte activation chunks per lane per tile
+constexpr int kOpsPerTile = kNT + kDmaOps;       // vector-memory ops per lane per tile
+constexpr int kScaleOps = kNT;                   // one scale word per n-tile per group of four tiles
 
-// grid (n blocks, max items) of 256 threads = 2 x 2 waves, one wave per SIMD
-// (the full register file: 4 x 8 MFMA 16x16x32 accumulators per wave plus a
-// four-deep ring of weight fragments).  Items hold up to 128 rows of one
-// expert.  A block covers 128 rows x 256 weight columns: GATEUP -> 128 output
-// columns (wave column wn: gate and up n-tiles of output columns 64*wn ..
-// 64*wn+63), otherwise 256 down columns (wave column wn: 8 n-tiles).
+// grid (n blocks, max items) of 512 threads = 2 x 4 waves, two waves per SIMD
+// (each wave: 4 x 4 MFMA 16x16x32 accumulators plus a four-deep ring of its
+// weight fragments, within half the register file, so one wave's loads,
+// dequantisation and LDS reads overlap the other's MFMAs).  Items hold up to
+// 128 rows of one expert.  A block covers 128 rows x 256 weight columns:
+// GATEUP -> 128 output columns (wave column wn: gate and up n-tiles of output
+// columns 32*wn .. 32*wn+31), otherwise 256 down columns (wave column wn: 4
+// n-tiles).
 //
 // Activation tiles (128 rows x 128 k, 32 KB) go from global memory straight
 // into LDS with the LDS-DMA load (global_load_lds_dwordx4) into a ring of
@@ -59,7 +65,7 @@ constexpr int kScaleOps = 8;      // one scale word per n-tile per group of four
 // b % 8 * ceil(total / 8) + b / 8, so consecutive logical blocks (the column
 // blocks of one item, then the next item of the same expert) share an L2.
 template <bool GATEUP>
-__global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
                                                              const int32_t* __restrict__ n_items,
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
   const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const ExpertPlanes pl = expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
   const uint64_t tstride = static_cast<uint64_t>(KT) * 1024;  // bytes between n-tiles
@@ -92,54 +98,56 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
   const uint8_t* sb0;
   const uint8_t* sb1;
   if (GATEUP) {
-    const int nt0 = nb * 8 + wn * 4;
+    const int nt0 = nb * 8 + wn * (kNT / 2);  // kNT/2 gate then kNT/2 up n-tiles of the same columns
     nb0 = eb + pl.gate_nib + nt0 * tstride;
     nb1 = eb + pl.up_nib + nt0 * tstride;
     sb0 = eb + pl.gate_sc + nt0 * sstride;
     sb1 = eb + pl.up_sc + nt0 * sstride;
   } else {
-    const int nt0 = nb * 16 + wn * 8;
+    const int nt0 = nb * 16 + wn * kNT;
     nb0 = eb + pl.down_nib + nt0 * tstride;
-    nb1 = nb0 + 4 * tstride;
+    nb1 = nb0 + (kNT / 2) * tstride;
     sb0 = eb + pl.down_sc + nt0 * sstride;
-    sb1 = sb0 + 4 * sstride;
+    sb1 = sb0 + (kNT / 2) * sstride;
   }
   nb0 += lane * 16;
   nb1 += lane * 16;
   sb0 += lane * 4;
   sb1 += lane * 4;
 
-  // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
+  // LDS-DMA sources: op q of wave w fills rows 32q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
-  const char* asrc[8];
+  const char* asrc[kDmaOps];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = 16 * q + 4 * wave + (lane >> 4);
+  for (int q = 0; q < kDmaOps; ++q) {
+    const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
     const int p = row0 + min(r, nrows - 1);
     const uint16_t* rowp = GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I;
     asrc[q] = reinterpret_cast<const char*>(rowp) + 16 * ((lane & 15) ^ (r & 15));
   }
 
-  u32x4 bq[kStages][8];
-  uint32_t sw[8], swn[8];
+  constexpr int kH = kNT / 2;
+  u32x4 bq[kStages][kNT];
+  uint32_t sw[kNT], swn[kNT];
   auto issue_tile = [&](int stage, int kt) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bq[stage][j] = ld16((j < 4 ? nb0 : nb1) + (j & 3) * tstride + kt * 1024);
+    for (int j = 0; j < kNT; ++j) bq[stage][j] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * 1024);
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][(16 * q + 4 * wave) * 128], 16, 0, 0);
+    for (int q = 0; q < kDmaOps; ++q)
+      __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
+                                       0, 0);
   };
   auto issue_scales = [&](uint32_t* dst, int grp) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      dst[j] = *reinterpret_cast<const uint32_t*>((j < 4 ? sb0 : sb1) + (j & 3) * sstride + grp * 256);
+    for (int j = 0; j < kNT; ++j)
+      dst[j] = *reinterpret_cast<const uint32_t*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + grp * 256);
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][kNT];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kNT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   issue_scales(sw, 0);
   issue_tile(0, 0);
@@ -171,9 +179,9 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
       if (kt + kAhead < KT) issue_tile((i + kAhead) % kStages, kt + kAhead);
       __builtin_amdgcn_sched_barrier(0);
 
-      float scf[8];
+      float scf[kNT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
+      for (int j = 0; j < kNT; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
       const uint16_t* abuf = As[i];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kNT; ++j) {
           const bf16x8 bv = dequant8(bq[i][j][s], scf[j]);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
@@ -191,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
     }
     if (!last) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sw[j] = swn[j];
+      for (int j = 0; j < kNT; ++j) sw[j] = swn[j];
     }
   }
 
@@ -200,22 +208,22 @@ __global__ __launch_bounds__(256, 1) void ffn_prefill_kernel(const uint16_t* __r
     const int rbase = wm * 64 + mt * 16 + 4 * g4;
     if (GATEUP) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = nb * 128 + wn * 64 + j * 16 + (lane & 15);
+      for (int j = 0; j < kH; ++j) {
+        const int col = nb * 128 + wn * (16 * kH) + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
           if (r < nrows) {
             const float gv = fminf(acc[mt][j][e], limit);
-            const float uv = fminf(fmaxf(acc[mt][j + 4][e], -limit), limit);
+            const float uv = fminf(fmaxf(acc[mt][j + kH][e], -limit), limit);
             h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
           }
         }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = nb * 256 + wn * 128 + j * 16 + (lane & 15);
+      for (int j = 0; j < kNT; ++j) {
+        const int col = nb * 256 + wn * (16 * kNT) + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
@@ -233,11 +241,11 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
                         hipStream_t s) {
   if (gateup) {
     dim3 g1(I / 128, max_items);
-    ffn_prefill_kernel<true><<<g1, 256, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h,
+    ffn_prefill_kernel<true><<<g1, kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h,
                                                 nullptr);
   } else {
     dim3 g2(H / 256, max_items);
-    ffn_prefill_kernel<false><<<g2, 256, 0, s>>>(act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
+    ffn_prefill_kernel<false><<<g2, kThreads, 0, s>>>(act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
                                                  out_rows);
   }
 }

@@ -29,13 +29,10 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
-constexpr int kAhead = 3;         // tiles in flight ahead of the one being multiplied
 constexpr int kWavesM = 2, kWavesN = 4;        // 8 waves: 2 along the rows x 4 along the columns
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kNT = 16 / kWavesN;                // weight n-tiles per wave
 constexpr int kDmaOps = 2048 / kThreads;         // 16-byte activation chunks per lane per tile
-constexpr int kOpsPerTile = kNT + kDmaOps;       // vector-memory ops per lane per tile
-constexpr int kScaleOps = kNT;                   // one scale word per n-tile per group of four tiles
 
 // grid (n blocks, max items) of 512 threads = 2 x 4 waves, two waves per SIMD
 // (each wave: 4 x 4 MFMA 16x16x32 accumulators plus a four-deep ring of its
@@ -54,11 +51,11 @@ constexpr int kScaleOps = kNT;                   // one scale word per n-tile pe
 // contiguous LDS, so the swizzle is applied on the global side: the lane that
 // lands in slot s of row r loads chunk s ^ (r & 15).
 //
-// Pipeline: tile kt+3 (weights into registers, then activations into LDS) is
-// issued while tile kt is multiplied; before tile kt the wave waits until at
-// most the ops of the later tiles (and one group of scale words) are still
-// outstanding, then the block barrier publishes every wave's DMA writes and
-// frees the stage that tile kt+3 reuses.
+// Pipeline, in pairs of k tiles: after the barrier before tiles kt, kt+1
+// (kt even), tiles kt+2 and kt+3 (weights into registers, then activations
+// into LDS) are issued into the two stages freed by tiles kt-2, kt-1, and stay
+// in flight while kt and kt+1 are multiplied; one barrier per pair halves the
+// block-wide synchronisation.
 //
 // Block order is remapped so the n blocks of one item run on the same XCD:
 // blocks go to the 8 XCDs round robin, and block b takes logical work
@@ -152,7 +149,6 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(const uint16_t
   issue_scales(sw, 0);
   issue_tile(0, 0);
   issue_tile(1, 1);
-  issue_tile(2, 2);
   __builtin_amdgcn_sched_barrier(0);
 
   const int arow = wm * 64 + (lane & 15);
@@ -163,21 +159,19 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(const uint16_t
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kt = 4 * u + i;
-      // Tile kt is complete once at most the ops issued after it are pending:
-      // tiles kt+1, kt+2, plus the scale words issued at the start of this
-      // group when that came after tile kt (i = 1, 2).  The last group drains.
-      if (last) {
+      // Every second tile: tiles kt and kt+1 (issued two tiles ago) are the
+      // last ops issued, so the wave drains its counter; the barrier then
+      // publishes all waves' DMA writes of both and frees the two stages of
+      // tiles kt-2, kt-1 for tiles kt+2, kt+3.
+      if ((i & 1) == 0) {
         wait_vmcnt<0>();
-      } else if (i == 1 || i == 2) {
-        wait_vmcnt<2 * kOpsPerTile + kScaleOps>();
-      } else {
-        wait_vmcnt<2 * kOpsPerTile>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 0 && !last) issue_scales(swn, u + 1);
+        if (kt + 2 < KT) issue_tile((i + 2) % kStages, kt + 2);
+        if (kt + 3 < KT) issue_tile((i + 3) % kStages, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (i == 0 && !last) issue_scales(swn, u + 1);
-      if (kt + kAhead < KT) issue_tile((i + kAhead) % kStages, kt + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
 
       float scf[kNT];
 #pragma unroll

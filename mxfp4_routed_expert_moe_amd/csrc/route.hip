@@ -84,6 +84,91 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const uint16_t* __res
   }
 }
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// Many-token regime on the float64 matrix cores (v_mfma_f64_16x16x4_f64).
+// part[hs][t][e] as above; grid (ceil(T/32), hsplit), 64 * E/64 threads
+// (E a multiple of 64).  Wave w owns experts 64w .. 64w+63 of 32 tokens: two
+// row tiles of 16 tokens x four column tiles of 16 experts, where column c of
+// tile j is expert 64w + 4c + j, so one 16-byte load gives a lane its four
+// tiles' router weights of one h.  The sum over h runs in chunks of 32: at
+// step s of a chunk, the lanes of k group g (lane / 16) supply
+// h = chunk + 8g + s for both operands (any assignment of h to (step, k) that
+// A and B share gives the same sum), so a lane loads its token's 8
+// consecutive x values with one 16-byte load and its experts' weights of
+// 8 rows with eight.  Products of bf16 x and float32 weights are exact in
+// float64.  Result layout of the instruction: lane l holds rows
+// 4r + l / 16, r = 0..3, of column l % 16.
+template <int MT>
+__global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* __restrict__ x, int T, int H,
+                                                                const float* __restrict__ W, int E, int hsplit,
+                                                                double* __restrict__ part) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * (16 * MT);
+  const int hlen = H / hsplit;
+  const int h0 = blockIdx.y * hlen + 8 * g;
+  const int e0 = 64 * wave + 4 * c;
+  const uint16_t* xr[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xr[m] = x + static_cast<size_t>(min(t0 + 16 * m + c, T - 1)) * H + h0;
+  const float* wr = W + static_cast<size_t>(h0) * E + e0;
+
+  f64x4 acc[MT][4];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  u32x4 xv[2][MT];
+  f32x4 wv[2][8];
+  auto load = [&](int b, int hc) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xv[b][m] = ld16(xr[m] + hc);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wv[b][s] = *reinterpret_cast<const f32x4*>(wr + static_cast<size_t>(hc + s) * E);
+  };
+  auto compute = [&](int b) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      double a[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const uint32_t word = xv[b][m][s >> 1];
+        a[m] = static_cast<double>(__uint_as_float((s & 1) ? (word & 0xffff0000u) : (word << 16)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const double bw = static_cast<double>(wv[b][s][j]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], bw, acc[m][j], 0, 0, 0);
+      }
+    }
+  };
+  // Two register buffers: the loads of chunk n+1 are in flight while chunk n
+  // is multiplied.
+  load(0, 0);
+  int hc = 0;
+  for (; hc + 64 <= hlen; hc += 64) {
+    load(1, hc + 32);
+    compute(0);
+    if (hc + 64 < hlen) load(0, hc + 64);
+    compute(1);
+  }
+  if (hc < hlen) compute(0);
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * m + 4 * r + g;
+      if (t < T) {
+        f64x4 v = {acc[m][0][r], acc[m][1][r], acc[m][2][r], acc[m][3][r]};
+        *reinterpret_cast<f64x4*>(part + (static_cast<size_t>(blockIdx.y) * T + t) * E + e0) = v;
+      }
+    }
+}
+
 // TPB tokens per block of 256 threads.  Thread e sums the hsplit partial
 // logits of expert e (fixed order) and writes s = sqrt(softplus(z)) and the
 // selection key s + bias to LDS; then wave w runs the top-k of token w: k
@@ -202,9 +287,9 @@ __global__ __launch_bounds__(256) void route_hash_kernel(const int32_t* __restri
 
 inline int route_tb(int T) { return T <= 256 ? 8 : 32; }
 
-// Number of h slices: enough blocks to cover the chip, with every wave's h
-// range (H / hsplit / 4) either 16, 32 or a multiple of 64.
-int route_hsplit(int T, int H) {
+// Number of h slices of the vector kernel: enough blocks to cover the chip,
+// with every wave's h range (H / hsplit / 4) either 16, 32 or a multiple of 64.
+static int route_hsplit_vector(int T, int H) {
   const int ntb = (T + route_tb(T) - 1) / route_tb(T);
   const int blocks = ntb * 4;  // E = 256 -> 4 expert blocks
   int hs = 1;
@@ -218,21 +303,47 @@ int route_hsplit(int T, int H) {
   return hs;
 }
 
+constexpr int kMfmaTokens = 32;  // tokens per block of the matrix-core kernel
+
+// Number of h slices of the matrix-core kernel: up to 1024 blocks (four
+// resident per CU), every slice a multiple of 32.
+static int route_hsplit_mfma(int T, int H) {
+  const int ntb = (T + kMfmaTokens - 1) / kMfmaTokens;
+  int hs = 1;
+  while (ntb * hs * 2 <= 1024 && (H / (hs * 2)) % 32 == 0) hs *= 2;
+  return hs;
+}
+
+// The matrix-core kernel takes many-token batches when E is a multiple of 64
+// and the router weights are 16-byte aligned (its weight loads are 16 bytes).
+static bool route_use_mfma(int T, int E, const float* w) {
+  return T > 256 && E % 64 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0;
+}
+
+int route_hsplit(int T, int H) { return max(route_hsplit_vector(T, H), route_hsplit_mfma(T, H)); }
+
 hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w, const float* bias, int E, int k,
                                 float scale, int32_t* ids, float* weights, double* part, hipStream_t s) {
-  const int hs = route_hsplit(T, H);
-  const int tb = route_tb(T);
-  const int hw = H / hs / 4;
-  dim3 g1((E + kExpBlock - 1) / kExpBlock, (T + tb - 1) / tb, hs);
-#define MOE_LOGITS(TB_, HC_) route_logits_kernel<TB_, HC_><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part)
-  if (tb == 8) {
-    if (hw == 16) MOE_LOGITS(8, 16);
-    else if (hw == 32) MOE_LOGITS(8, 32);
-    else MOE_LOGITS(8, 64);
+  int hs;
+  if (route_use_mfma(T, E, w)) {
+    hs = route_hsplit_mfma(T, H);
+    dim3 g1((T + kMfmaTokens - 1) / kMfmaTokens, hs);
+    route_logits_mfma_kernel<kMfmaTokens / 16><<<g1, 64 * (E / 64), 0, s>>>(x, T, H, w, E, hs, part);
   } else {
-    MOE_LOGITS(32, 16);  // compute-bound regime: a short chunk keeps registers for the 32 token sums
-  }
+    hs = route_hsplit_vector(T, H);
+    const int tb = route_tb(T);
+    const int hw = H / hs / 4;
+    dim3 g1((E + kExpBlock - 1) / kExpBlock, (T + tb - 1) / tb, hs);
+#define MOE_LOGITS(TB_, HC_) route_logits_kernel<TB_, HC_><<<g1, 256, 0, s>>>(x, T, H, w, E, hs, part)
+    if (tb == 8) {
+      if (hw == 16) MOE_LOGITS(8, 16);
+      else if (hw == 32) MOE_LOGITS(8, 32);
+      else MOE_LOGITS(8, 64);
+    } else {
+      MOE_LOGITS(32, 16);  // compute-bound regime: a short chunk keeps registers for the 32 token sums
+    }
 #undef MOE_LOGITS
+  }
   if (T <= 256) route_topk_kernel<1><<<T, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   else route_topk_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   return hipGetLastError();

@@ -204,6 +204,45 @@ def test_ffn_phases_equal_one_call(T):
     assert torch.equal(layer.out_rows[:n], ref[:n])
 
 
+# Many-token learned routing: 16-byte aligned router weights with E a
+# multiple of 64 take the float64 matrix-core logits kernel; the same weights
+# 4 bytes off that alignment take the vector-unit kernel.  Both must give the
+# oracle's ids bit for bit and its weights, and each other's ids.
+ROUTER_SHAPES = [
+    # (T, H, E, bias)
+    (257, 512, 64, True),      # one token past the many-token threshold, ragged 32-token blocks
+    (300, 1024, 128, False),
+    (1000, 4096, 256, True),   # full hidden size and expert count
+]
+
+
+@pytest.mark.parametrize("T,H,E,bias", ROUTER_SHAPES)
+def test_router_kernels_many_tokens(T, H, E, bias):
+    print(f"[parity] router T={T} H={H} E={E} bias={bias}", flush=True)
+    seed = 3000 + T
+    x = WL.make_x(seed, T, H)
+    router = WL.make_router(seed, H, E)
+    b = (np.random.default_rng(seed).standard_normal(E) * 0.5).astype(np.float32) if bias else None
+    ids_ref, w_ref, _ = O.route_learned(x, router, b, 6, WL.ROUTE_SCALE)
+    gap = O.boundary_gap(x, router, b, 6)
+    xd = LC.dev(x)
+    bd = None if b is None else LC.dev(b)
+    aligned = LC.dev(router.reshape(-1))
+    assert aligned.data_ptr() % 16 == 0
+    off = torch.empty(H * E + 1, dtype=torch.float32, device="cuda")
+    off[1:] = aligned
+    shifted = off[1:]
+    assert shifted.data_ptr() % 16 == 4
+    got = {}
+    for name, w in (("matrix", aligned), ("vector", shifted)):
+        ids, wts = B.route(xd, T, E, 6, WL.ROUTE_SCALE, w_router=w, sel_bias=bd)
+        torch.cuda.synchronize()
+        got[name] = dict(ids=LC.host(ids), weights=LC.host(wts))
+        LC.check_routing(got[name], ids_ref, w_ref, gap)
+    clear = gap >= LC.AMBIGUOUS_GAP
+    assert np.array_equal(got["matrix"]["ids"][clear], got["vector"]["ids"][clear])
+
+
 def test_hash_out_of_range_token_gives_dropped_ids():
     E = 16
     table, tok = WL.make_hash(3, 10, E, 6, vocab=50)

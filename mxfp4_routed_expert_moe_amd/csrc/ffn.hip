@@ -8,21 +8,18 @@
 // MXFP4 bytes stream from HBM in the tiled device layout: one 16-byte load per
 // lane gives the 32 codes of one column for one 128-wide k tile, and the
 // hardware scaled convert turns 8 codes and their E8M0 scale into the 8 bf16
-// of one 16x16x32 MFMA B fragment.  Nothing is ever dequantised to memory.
-//
-// Work is a device-side list of items (group, first row, row count) built
-// from the dispatch offsets, so the host never learns the per-expert counts:
-// the grid covers the worst case and surplus blocks return at once.
+// of one MFMA B fragment.  Nothing is ever dequantised to memory.
 //
 // Two kernel families (ffn_decode.hip, ffn_prefill.hip):
-//  * decode (few rows per expert, HBM bound): the four waves of a block split
-//    the K axis and share one set of 16-row tiles; each wave streams its
-//    quarter of the block's weight columns with 16-byte loads one k tile
-//    ahead, and the partial sums meet in LDS in a fixed order;
-//  * prefill (many rows per expert, MFMA bound): 128-row tiles of the
-//    gathered activations go through LDS (row pitch padded so that MFMA
-//    fragment reads are bank-conflict free), double buffered; each wave owns
-//    a 64 x 64 output tile and reads its weight fragments straight from HBM.
+//  * decode (few rows per expert, HBM bound): a block takes one routed expert
+//    straight from the dispatch offsets, or one 16-row chunk of the shared
+//    group; its four waves split the K axis and the partial sums meet in LDS
+//    in a fixed order;
+//  * prefill (many rows per expert, MFMA bound): a device-side work list of
+//    items (group, first row, row count) of at most 64 rows, built here from
+//    the offsets so the host never learns the per-expert counts; the grid
+//    covers the worst case and surplus blocks return at once.  Activation
+//    tiles go to LDS by DMA, weight fragments straight to registers.
 #include "ffn_internal.h"
 
 namespace moe {

@@ -14,7 +14,7 @@ struct FfnWs {
 };
 
 constexpr int kDecodeRows = 16;    // rows per decode item
-constexpr int kPrefillRows = 128;  // rows per prefill item
+constexpr int kPrefillRows = 64;   // rows per prefill item
 
 // K sizes with a compiled decode variant (k tiles per wave: K / 512 with
 // four K-splitting waves, one of 1, 2, 4, 8).

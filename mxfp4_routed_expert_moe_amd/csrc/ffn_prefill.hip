@@ -1,5 +1,5 @@
 // Expert FFN, prefill family (many rows per expert; MFMA bound).  Same
-// arithmetic as the decode family over items of up to 128 rows
+// arithmetic as the decode family over items of up to 64 rows
 // ("Model techniques map -- DeepSeek-V4-Flash", row "SwiGLU feed-forward").
 #include "ffn_internal.h"
 
@@ -29,21 +29,21 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
-constexpr int kWavesM = 2, kWavesN = 4;        // 8 waves: 2 along the rows x 4 along the columns
+constexpr int kWavesM = 1, kWavesN = 4;        // 4 waves side by side along the columns
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kNT = 16 / kWavesN;                // weight n-tiles per wave
-constexpr int kDmaOps = 2048 / kThreads;         // 16-byte activation chunks per lane per tile
+constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chunks per lane per tile
 
-// grid (n blocks, max items) of 512 threads = 2 x 4 waves, two waves per SIMD
-// (each wave: 4 x 4 MFMA 16x16x32 accumulators plus a four-deep ring of its
-// weight fragments, within half the register file, so one wave's loads,
-// dequantisation and LDS reads overlap the other's MFMAs).  Items hold up to
-// 128 rows of one expert.  A block covers 128 rows x 256 weight columns:
-// GATEUP -> 128 output columns (wave column wn: gate and up n-tiles of output
-// columns 32*wn .. 32*wn+31), otherwise 256 down columns (wave column wn: 4
-// n-tiles).
+// grid (n blocks, max items) of 256 threads = 4 waves side by side, two
+// blocks per CU (64 KB of LDS each), so two waves per SIMD: each wave has 4 x 4
+// MFMA 16x16x32 accumulators plus a four-deep ring of its weight fragments
+// within half the register file, and one block's barriers, pipeline fill and
+// epilogue overlap the other block's MFMAs.  Items hold up to 64 rows of one
+// expert.  A block covers 64 rows x 256 weight columns: GATEUP -> 128 output
+// columns (wave wn: gate and up n-tiles of output columns 32*wn .. 32*wn+31),
+// otherwise 256 down columns (wave wn: 4 n-tiles).
 //
-// Activation tiles (128 rows x 128 k, 32 KB) go from global memory straight
+// Activation tiles (64 rows x 128 k, 16 KB) go from global memory straight
 // into LDS with the LDS-DMA load (global_load_lds_dwordx4) into a ring of
 // four stages.  Row r of a tile occupies 256 bytes; its 16-byte chunk c sits
 // at slot c ^ (r & 15), so an MFMA fragment read (16 rows, same chunk) hits 16
@@ -62,7 +62,7 @@ constexpr int kDmaOps = 2048 / kThreads;         // 16-byte activation chunks pe
 // b % 8 * ceil(total / 8) + b / 8, so consecutive logical blocks (the column
 // blocks of one item, then the next item of the same expert) share an L2.
 template <bool GATEUP>
-__global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
+__global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
                                                              const int32_t* __restrict__ n_items,
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_prefill_kernel(const uint16_t
   sb0 += lane * 4;
   sb1 += lane * 4;
 
-  // LDS-DMA sources: op q of wave w fills rows 32q + 4w + lane/16.  Rows past
+  // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
   const char* asrc[kDmaOps];
 #pragma unroll

@@ -44,7 +44,7 @@ SMALL = [
     (29, 1024, 512, 32, "learned", True),     # decode, MT=2, selection bias
     (37, 512, 512, 16, "learned", False),     # decode, MT=4 (shared group spans 3 m-tiles)
     (61, 512, 512, 16, "hash", False),        # hash routing
-    (300, 512, 512, 16, "learned", False),    # prefill, ragged 128-row tiles
+    (300, 512, 512, 16, "learned", False),    # prefill, ragged 64-row items
     (700, 512, 512, 256, "learned", False),   # prefill, 256 experts, many tiny groups
     (64, 512, 512, 256, "learned", True),     # decode with 256 experts, many empty
 ]

@@ -11,9 +11,8 @@
 //  2. per expert (one wave): exclusive scan of its counts over the chunks;
 //  3. per chunk: exclusive scan of the expert totals -> offsets, then every
 //     pair's row = offsets[e] + chunk base + rank, and the shared rows.
-// Small batches (T * k <= 2048) take one single-block kernel with the same
-// result: counts, scan, and each pair's rank among the earlier pairs of its
-// expert counted directly.
+// Small batches (T * k <= 2048, E <= 256) take one single-block kernel with
+// the same result (ranks from wave ballots and per-chunk prefix counts).
 #include "moe_internal.h"
 
 namespace moe {
@@ -120,24 +119,70 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const int32_t* __
 }
 
 constexpr int kSmallPairs = 2048;
+constexpr int kSmallExperts = 256;
+constexpr int kSmallChunks = kSmallPairs / 64;
 
+// One 1024-thread block, T * k <= 2048 pairs, E <= 256.  Pair i is handled by
+// thread i mod 1024 and belongs to 64-pair chunk i / 64, one wave's worth.
+// Its rank among the earlier pairs of its expert = (pairs of that expert in
+// earlier chunks) + (lanes below it in its own chunk with the same expert).
+// The second term comes from ballots: the wave repeatedly takes the expert of
+// its lowest unmatched lane and matches all lanes holding it, so the loop runs
+// once per distinct expert of the chunk.  The first lane of each match writes
+// the chunk's count of that expert; per-expert prefix sums over the chunks
+// then give the first term.  No atomics, no order-dependent step.
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_token,
                                                               int32_t* __restrict__ slot_row) {
-  __shared__ int sid[kSmallPairs];
-  __shared__ int cnt[1024];
+  __shared__ int cnt[kSmallExperts];
+  __shared__ unsigned short pre[kSmallChunks][kSmallExperts];
   __shared__ int tmp[16];
   const int n = T * k;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < E; i += 1024) cnt[i] = 0;
-  for (int i = tid; i < n; i += 1024) {
-    const int e = ids[i];
-    sid[i] = (e >= 0 && e < E) ? e : -1;
+  const int nch = (n + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < nch * kSmallExperts; i += 1024) (&pre[0][0])[i] = 0;
+  __syncthreads();
+
+  int ex[2], rk[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int i = tid + 1024 * p;
+    const int c = wave + 16 * p;
+    ex[p] = -1;
+    rk[p] = 0;
+    if (c >= nch) continue;  // wave-uniform
+    int e = i < n ? ids[i] : -1;
+    if (e >= E) e = -1;
+    ex[p] = e;
+    // Branch-free body: every lane evaluates the match; only the matched
+    // lanes keep its rank and count.
+    uint64_t todo = __ballot(e >= 0);
+    int r = 0, cm = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int el = __builtin_amdgcn_readlane(e, leader);
+      const uint64_t m = __ballot(e == el);
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+      const bool mine = e == el;
+      r = mine ? below : r;
+      cm = mine ? __builtin_popcountll(m) : cm;
+      todo &= ~m;
+    }
+    rk[p] = r;
+    if (e >= 0 && r == 0) pre[c][e] = static_cast<unsigned short>(cm);
   }
   __syncthreads();
-  for (int i = tid; i < n; i += 1024)
-    if (sid[i] >= 0) atomicAdd(&cnt[sid[i]], 1);  // integer counts: order does not matter
+  if (tid < E) {
+    int run = 0;
+    for (int c = 0; c < nch; ++c) {
+      const int v = pre[c][tid];
+      pre[c][tid] = static_cast<unsigned short>(run);
+      run += v;
+    }
+    cnt[tid] = run;
+  }
   __syncthreads();
   const int n_routed = block_excl_scan_1024(cnt, E, tmp);
   for (int i = tid; i < E; i += 1024) offsets[i] = cnt[i];
@@ -145,14 +190,14 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
     offsets[E] = n_routed;
     offsets[E + 1] = n_routed + T;
   }
-  for (int i = tid; i < n; i += 1024) {
-    const int e = sid[i];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int i = tid + 1024 * p;
+    if (i >= n) continue;
     const int t = i / k, j = i - t * k;
     int32_t row = -1;
-    if (e >= 0) {
-      int r = 0;
-      for (int q = 0; q < i; ++q) r += (sid[q] == e) ? 1 : 0;
-      row = cnt[e] + r;
+    if (ex[p] >= 0) {
+      row = cnt[ex[p]] + pre[wave + 16 * p][ex[p]] + rk[p];
       row_token[row] = t;
     }
     slot_row[static_cast<size_t>(t) * (k + 1) + j] = row;
@@ -173,7 +218,7 @@ size_t dispatch_ws_bytes(int T, int E, int k) {
 
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t s) {
-  if (T * k <= kSmallPairs) {
+  if (T * k <= kSmallPairs && E <= kSmallExperts) {
     dispatch_small_kernel<<<1, 1024, 0, s>>>(ids, T, E, k, offsets, row_token, slot_row);
     return hipGetLastError();
   }

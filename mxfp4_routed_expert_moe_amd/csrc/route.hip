@@ -169,11 +169,57 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
     }
 }
 
+// One step of a wave arg-max: take the (key, id) of the lane that DPP
+// control CTRL pairs with this one when it is larger, or equal with a lower
+// id (the same order as the top-k).
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp_step(double& bk, int& be) {
+  const uint64_t bits = __builtin_bit_cast(uint64_t, bk);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(bits), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(bits >> 32), CTRL, 0xF, 0xF, false);
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  const double ok = __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+  if (ok > bk || (ok == bk && oe < be)) {
+    bk = ok;
+    be = oe;
+  }
+}
+
+// Arg-max of (key descending, id ascending) over the 64 lanes; every lane
+// gets the result.  Within each row of 16 lanes four DPP exchanges (lane ^ 1,
+// lane ^ 2, then the half-row and row mirrors) leave the row's best in all its
+// lanes; the four row results are then read as uniform values and compared.
+// No LDS round trips, unlike a shuffle butterfly.
+__device__ __forceinline__ void wave_argmax(double& bk, int& be) {
+  argmax_dpp_step<0xB1>(bk, be);   // quad_perm [1,0,3,2]
+  argmax_dpp_step<0x4E>(bk, be);   // quad_perm [2,3,0,1]
+  argmax_dpp_step<0x141>(bk, be);  // row_half_mirror
+  argmax_dpp_step<0x140>(bk, be);  // row_mirror
+  const uint64_t bits = __builtin_bit_cast(uint64_t, bk);
+  const uint32_t lo = static_cast<uint32_t>(bits), hi = static_cast<uint32_t>(bits >> 32);
+  double rk = __builtin_bit_cast(double, (static_cast<uint64_t>(__builtin_amdgcn_readlane(hi, 0)) << 32) |
+                                             static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 0)));
+  int re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const double ok = __builtin_bit_cast(
+        double, (static_cast<uint64_t>(__builtin_amdgcn_readlane(hi, 16 * r)) << 32) |
+                    static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 16 * r)));
+    const int oe = __builtin_amdgcn_readlane(be, 16 * r);
+    if (ok > rk || (ok == rk && oe < re)) {
+      rk = ok;
+      re = oe;
+    }
+  }
+  bk = rk;
+  be = re;
+}
+
 // TPB tokens per block of 256 threads.  Thread e sums the hsplit partial
 // logits of expert e (fixed order) and writes s = sqrt(softplus(z)) and the
 // selection key s + bias to LDS; then wave w runs the top-k of token w: k
 // rounds of a wave-wide argmax over (key descending, expert id ascending),
-// and the weights from the unbiased s.
+// and the weights from the unbiased s of the chosen ids.
 template <int TPB>
 __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restrict__ part, int T, int E, int hsplit,
                                                          const float* __restrict__ bias, int k, float scale,
@@ -211,14 +257,13 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
   if (q >= TPB) return;
   const int t = tb + q;
   if (t >= T) return;
-  double key[4], sc[4];
+  double key[4];
   bool live[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int ee = lane + 64 * u;
     live[u] = ee < E;
     key[u] = live[u] ? s_key[q][ee] : -INFINITY;
-    sc[u] = live[u] ? s_sc[q][ee] : 0.0;
   }
   int sel_id[8];
   double sel_s[8];
@@ -227,7 +272,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
     sel_id[j] = 0x7fffffff;
     sel_s[j] = 0.0;
     if (j >= k) continue;
-    double bk = -INFINITY, bs = 0.0;
+    double bk = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -235,22 +280,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
       if (live[u] && (key[u] > bk || (key[u] == bk && ee < be))) {
         bk = key[u];
         be = ee;
-        bs = sc[u];
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ok = __shfl_xor(bk, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const double os = __shfl_xor(bs, off, 64);
-      if (ok > bk || (ok == bk && oe < be)) {
-        bk = ok;
-        be = oe;
-        bs = os;
-      }
-    }
+    wave_argmax(bk, be);
     sel_id[j] = be;
-    sel_s[j] = bs;
+    if (be != 0x7fffffff) sel_s[j] = s_sc[q][be];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (be == lane + 64 * u) live[u] = false;

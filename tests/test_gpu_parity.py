@@ -243,6 +243,30 @@ def test_router_kernels_many_tokens(T, H, E, bias):
     assert np.array_equal(got["matrix"]["ids"][clear], got["vector"]["ids"][clear])
 
 
+@pytest.mark.parametrize("T", [40, 300])   # decode-size and many-token logits kernels
+def test_router_exact_ties_go_to_the_lower_id(T):
+    """Three router columns made identical (and large) give three equal keys
+    inside the top 6 for about half of the tokens; the ids must come out in
+    ascending order among them, as the oracle orders equal keys."""
+    print(f"[parity] router ties T={T}", flush=True)
+    H, E = 512, 256
+    seed = 4000 + T
+    x = WL.make_x(seed, T, H)
+    router = WL.make_router(seed, H, E)
+    router[:, 7] *= 10.0
+    router[:, 130] = router[:, 7]
+    router[:, 201] = router[:, 7]
+    ids_ref, w_ref, _ = O.route_learned(x, router, None, 6, WL.ROUTE_SCALE)
+    gap = O.boundary_gap(x, router, None, 6)
+    ids, wts = B.route(LC.dev(x), T, E, 6, WL.ROUTE_SCALE, w_router=LC.dev(router))
+    torch.cuda.synchronize()
+    g = dict(ids=LC.host(ids), weights=LC.host(wts))
+    LC.check_routing(g, ids_ref, w_ref, gap)
+    tied = (ids_ref[:, :3] == np.array([7, 130, 201])).all(axis=1)
+    assert tied.sum() >= T // 4, "the tie case did not occur often enough to test it"  # 15 of 40, 113 of 300
+    assert (g["ids"][tied, :3] == np.array([7, 130, 201])).all()
+
+
 def test_hash_out_of_range_token_gives_dropped_ids():
     E = 16
     table, tok = WL.make_hash(3, 10, E, 6, vocab=50)

@@ -172,17 +172,24 @@ __global__ __launch_bounds__(256) void route_logits_mfma_kernel(const uint16_t* 
 // One step of a wave arg-max: take the (key, id) of the lane that DPP
 // control CTRL pairs with this one when it is larger, or equal with a lower
 // id (the same order as the top-k).
+// (ok, oe) precedes (bk, be) in the top-k order: larger key, or equal key and
+// lower id.  Bitwise operators keep it branch-free (no exec-mask juggling).
+__device__ __forceinline__ bool precedes(double ok, int oe, double bk, int be) {
+  return (ok > bk) | ((ok == bk) & (oe < be));
+}
+
+// One step of a wave arg-max: take the (key, id) of the lane that DPP
+// control CTRL pairs with this one when it precedes this lane's.
 template <int CTRL>
 __device__ __forceinline__ void argmax_dpp_step(double& bk, int& be) {
   const uint64_t bits = __builtin_bit_cast(uint64_t, bk);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(bits), CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(bits >> 32), CTRL, 0xF, 0xF, false);
-  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp(static_cast<int>(bits), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp(static_cast<int>(bits >> 32), CTRL, 0xF, 0xF, false);
+  const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xF, 0xF, false);
   const double ok = __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-  if (ok > bk || (ok == bk && oe < be)) {
-    bk = ok;
-    be = oe;
-  }
+  const bool take = precedes(ok, oe, bk, be);
+  bk = take ? ok : bk;
+  be = take ? oe : be;
 }
 
 // Arg-max of (key descending, id ascending) over the 64 lanes; every lane
@@ -206,10 +213,9 @@ __device__ __forceinline__ void wave_argmax(double& bk, int& be) {
         double, (static_cast<uint64_t>(__builtin_amdgcn_readlane(hi, 16 * r)) << 32) |
                     static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 16 * r)));
     const int oe = __builtin_amdgcn_readlane(be, 16 * r);
-    if (ok > rk || (ok == rk && oe < re)) {
-      rk = ok;
-      re = oe;
-    }
+    const bool take = precedes(ok, oe, rk, re);
+    rk = take ? ok : rk;
+    re = take ? oe : re;
   }
   bk = rk;
   be = re;
@@ -277,17 +283,15 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const double* __restric
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int ee = lane + 64 * u;
-      if (live[u] && (key[u] > bk || (key[u] == bk && ee < be))) {
-        bk = key[u];
-        be = ee;
-      }
+      const bool take = live[u] & precedes(key[u], ee, bk, be);
+      bk = take ? key[u] : bk;
+      be = take ? ee : be;
     }
     wave_argmax(bk, be);
     sel_id[j] = be;
     if (be != 0x7fffffff) sel_s[j] = s_sc[q][be];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (be == lane + 64 * u) live[u] = false;
+    for (int u = 0; u < 4; ++u) live[u] = live[u] & (be != lane + 64 * u);
   }
   if (lane == 0) {
     double sum = 0.0;

@@ -221,37 +221,56 @@ __device__ __forceinline__ void wave_argmax(double& bk, int& be) {
   be = re;
 }
 
-// TPB tokens per block of 256 threads.  Thread e sums the hsplit partial
-// logits of expert e (fixed order) and writes s = sqrt(softplus(z)) and the
+// TPB tokens per block of 256 * SPLIT threads.  The SPLIT threads of expert e
+// sum interleaved subsets of its hsplit partial logits, which are then added
+// in a fixed order; thread e writes s = sqrt(softplus(z)) and the
 // selection key s + bias to LDS; then wave w runs the top-k of token w: k
 // rounds of a wave-wide argmax over (key descending, expert id ascending),
 // and the weights from the unbiased s of the chosen ids.
-template <int TPB>
-__global__ __launch_bounds__(256) void route_topk_kernel(const double* __restrict__ part, int T, int E, int hsplit,
-                                                         const float* __restrict__ bias, int k, float scale,
-                                                         int32_t* __restrict__ ids, float* __restrict__ weights) {
+template <int TPB, int SPLIT>
+__global__ __launch_bounds__(256 * SPLIT) void route_topk_kernel(const double* __restrict__ part, int T, int E,
+                                                                 int hsplit, const float* __restrict__ bias, int k,
+                                                                 float scale, int32_t* __restrict__ ids,
+                                                                 float* __restrict__ weights) {
   __shared__ double s_key[TPB][256];
   __shared__ double s_sc[TPB][256];
-  const int e = threadIdx.x;
+  __shared__ double s_part[SPLIT][TPB][256];
+  const int e = threadIdx.x & 255;
+  const int qs = threadIdx.x >> 8;  // which of the SPLIT threads of expert e
   const int tb = blockIdx.x * TPB;
+  const size_t stride = static_cast<size_t>(T) * E;
   if (e < E) {
+#pragma unroll
+    for (int q = 0; q < TPB; ++q) {
+      const int t = tb + q;
+      if (t >= T) break;
+      // Slices qs, qs + SPLIT, ... in increasing order, eight loads in flight.
+      const double* pp = part + static_cast<size_t>(qs) * stride + static_cast<size_t>(t) * E + e;
+      const size_t step = static_cast<size_t>(SPLIT) * stride;
+      const int cnt = qs < hsplit ? (hsplit - qs + SPLIT - 1) / SPLIT : 0;
+      double z = 0.0;
+      int i = 0;
+      for (; i + 8 <= cnt; i += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pp[(i + u) * step];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) z += v[u];
+      }
+      for (; i < cnt; ++i) z += pp[i * step];
+      s_part[qs][q][e] = z;
+    }
+  }
+  if (SPLIT > 1) __syncthreads();
+  if (qs == 0 && e < E) {
     const double b = bias ? static_cast<double>(bias[e]) : 0.0;
 #pragma unroll
     for (int q = 0; q < TPB; ++q) {
       const int t = tb + q;
       if (t >= T) break;
-      double z = 0.0;
-      const double* pp = part + static_cast<size_t>(t) * E + e;
-      const size_t stride = static_cast<size_t>(T) * E;
-      int hs = 0;
-      for (; hs + 8 <= hsplit; hs += 8) {
-        double v[8];
+      double z = s_part[0][q][e];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = pp[(hs + u) * stride];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) z += v[u];
-      }
-      for (; hs < hsplit; ++hs) z += pp[hs * stride];
+      for (int r = 1; r < SPLIT; ++r) z += s_part[r][q][e];
       const double sc = sqrt(fmax(z, 0.0) + log1p(exp(-fabs(z))));
       s_sc[q][e] = sc;
       s_key[q][e] = sc + b;
@@ -382,8 +401,11 @@ hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w,
     }
 #undef MOE_LOGITS
   }
-  if (T <= 256) route_topk_kernel<1><<<T, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
-  else route_topk_kernel<4><<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
+  // Few tokens: one token per block (many slices when very few: four threads
+  // per expert share them).  Many tokens: four tokens per block.
+  if (T <= 256 && hs >= 32) route_topk_kernel<1, 4><<<T, 1024, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
+  else if (T <= 256) route_topk_kernel<1, 1><<<T, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
+  else route_topk_kernel<4, 1><<<(T + 3) / 4, 256, 0, s>>>(part, T, E, hs, bias, k, scale, ids, weights);
   return hipGetLastError();
 }
 

@@ -204,12 +204,16 @@ def test_ffn_phases_equal_one_call(T):
     assert torch.equal(layer.out_rows[:n], ref[:n])
 
 
-# Many-token learned routing: 16-byte aligned router weights with E a
-# multiple of 64 take the float64 matrix-core logits kernel; the same weights
-# 4 bytes off that alignment take the vector-unit kernel.  Both must give the
-# oracle's ids bit for bit and its weights, and each other's ids.
+# Learned routing on each logits kernel: up to 256 tokens take the vector-unit
+# kernel; more tokens with 16-byte aligned router weights (E a multiple of 64)
+# take the float64 matrix-core kernel, and the same weights 4 bytes off that
+# alignment the vector-unit kernel.  All must give the oracle's ids bit for bit
+# and its weights, and each other's ids.
 ROUTER_SHAPES = [
     # (T, H, E, bias)
+    (3, 512, 16, False),       # a ragged 8-token block, few experts
+    (40, 1024, 64, True),
+    (200, 4096, 256, False),   # full hidden size and expert count, few tokens
     (257, 512, 64, True),      # one token past the many-token threshold, ragged 32-token blocks
     (300, 1024, 128, False),
     (1000, 4096, 256, True),   # full hidden size and expert count
@@ -234,13 +238,13 @@ def test_router_kernels_many_tokens(T, H, E, bias):
     shifted = off[1:]
     assert shifted.data_ptr() % 16 == 4
     got = {}
-    for name, w in (("matrix", aligned), ("vector", shifted)):
+    for name, w in (("aligned", aligned), ("vector", shifted)):
         ids, wts = B.route(xd, T, E, 6, WL.ROUTE_SCALE, w_router=w, sel_bias=bd)
         torch.cuda.synchronize()
         got[name] = dict(ids=LC.host(ids), weights=LC.host(wts))
         LC.check_routing(got[name], ids_ref, w_ref, gap)
     clear = gap >= LC.AMBIGUOUS_GAP
-    assert np.array_equal(got["matrix"]["ids"][clear], got["vector"]["ids"][clear])
+    assert np.array_equal(got["aligned"]["ids"][clear], got["vector"]["ids"][clear])
 
 
 @pytest.mark.parametrize("T", [40, 300])   # decode-size and many-token logits kernels

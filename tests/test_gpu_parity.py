@@ -243,6 +243,9 @@ def test_router_kernels_many_tokens(T, H, E, bias):
         torch.cuda.synchronize()
         got[name] = dict(ids=LC.host(ids), weights=LC.host(wts))
         LC.check_routing(got[name], ids_ref, w_ref, gap)
+        # the six weights of a token sum to the route scale (float32 weights, summed exactly)
+        wsum = got[name]["weights"].astype(np.float64).sum(axis=1)
+        assert np.max(np.abs(wsum - WL.ROUTE_SCALE)) <= 4 * np.spacing(np.float32(WL.ROUTE_SCALE))
     clear = gap >= LC.AMBIGUOUS_GAP
     assert np.array_equal(got["aligned"]["ids"][clear], got["vector"]["ids"][clear])
 
@@ -269,6 +272,29 @@ def test_router_exact_ties_go_to_the_lower_id(T):
     tied = (ids_ref[:, :3] == np.array([7, 130, 201])).all(axis=1)
     assert tied.sum() >= T // 4, "the tie case did not occur often enough to test it"  # 15 of 40, 113 of 300
     assert (g["ids"][tied, :3] == np.array([7, 130, 201])).all()
+
+
+@pytest.mark.parametrize("T", [24, 300])   # decode-size and many-token logits kernels
+def test_forced_routing_by_bias(T):
+    """A +1e6 selection bias on six chosen experts selects exactly those for
+    every token, ordered by their unbiased scores, with weights from the
+    unbiased scores."""
+    print(f"[parity] forced routing T={T}", flush=True)
+    H, E = 1024, 256
+    seed = 6000 + T
+    x = WL.make_x(seed, T, H)
+    router = WL.make_router(seed, H, E)
+    chosen = np.array([3, 77, 100, 101, 200, 255])
+    b = np.zeros(E, dtype=np.float32)
+    b[chosen] = 1e6
+    ids_ref, w_ref, _ = O.route_learned(x, router, b, 6, WL.ROUTE_SCALE)
+    gap = O.boundary_gap(x, router, b, 6)
+    assert (np.sort(ids_ref, axis=1) == chosen).all()
+    ids, wts = B.route(LC.dev(x), T, E, 6, WL.ROUTE_SCALE, w_router=LC.dev(router), sel_bias=LC.dev(b))
+    torch.cuda.synchronize()
+    g = dict(ids=LC.host(ids), weights=LC.host(wts))
+    assert (np.sort(g["ids"], axis=1) == chosen).all()
+    LC.check_routing(g, ids_ref, w_ref, gap)
 
 
 def test_hash_out_of_range_token_gives_dropped_ids():

@@ -40,7 +40,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode_t64")
     p.add_argument("--copies", type=int, default=4, help="expert blob copies rotated across steps")
-    p.add_argument("--cpu-sample-tokens", type=int, default=16)
+    p.add_argument("--cpu-sample-tokens", type=int, default=40,
+                   help="tokens of the workload the CPU oracle runs on (about 10-15 s of work)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size first (to scale HBM counters)")

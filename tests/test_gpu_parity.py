@@ -18,7 +18,7 @@ from tests import layer_check as LC  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def _small_inputs(T, hidden, inter, E, seed, routing="learned", bias=False):
+def _small_inputs(T, hidden, inter, E, seed, routing="learned", bias=False, top_k=6):
     w = WL.Workload(90, "small", T, routing, None)
     x = WL.make_x(seed, T, hidden)
     router = b = table = tok = None
@@ -27,9 +27,9 @@ def _small_inputs(T, hidden, inter, E, seed, routing="learned", bias=False):
         if bias:
             b = (np.random.default_rng(seed).standard_normal(E) * 0.5).astype(np.float32)
     else:
-        table, tok = WL.make_hash(seed, T, E, 6, vocab=1000)
+        table, tok = WL.make_hash(seed, T, E, top_k, vocab=1000)
     experts = WL.make_experts(seed, E + 1, hidden, inter)
-    return WL.LayerInputs(w, x, router, b, table, tok, experts, hidden, inter, E, 6)
+    return WL.LayerInputs(w, x, router, b, table, tok, experts, hidden, inter, E, top_k)
 
 
 def _experts(inp):
@@ -62,6 +62,23 @@ def test_layer_small_shapes(T, H, I, E, routing, bias):
                       limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table)
     n = int(ref["offsets"][-1])
     LC.assert_output_close(LC.host(g["out_rows"][:n]), ref["out_rows"], "all rows")
+    LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
+
+
+@pytest.mark.parametrize("T,E,top_k,routing", [
+    (20, 100, 1, "learned"),    # one expert per token, E not a multiple of 64 (or of 16)
+    (20, 100, 8, "learned"),    # the largest top_k
+    (150, 48, 8, "learned"),    # prefill kernels (T*(k+1) > 16*(E+1)), largest top_k
+    (400, 48, 1, "hash"),       # prefill kernels with one routed row per token
+])
+def test_top_k_and_expert_count_extremes(T, E, top_k, routing):
+    print(f"[parity] top_k={top_k} E={E} T={T} {routing}", flush=True)
+    inp = _small_inputs(T, 512, 512, E, 7000 + T + top_k, routing, top_k=top_k)
+    r = LC.full_check(inp, _experts(inp))
+    assert r["ambiguous"] == 0
+    g = r["g"]
+    ref = O.moe_layer(inp.x, inp.experts, n_experts=E, hidden=512, inter=512, top_k=top_k, route_scale=1.5,
+                      limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table)
     LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
 
 

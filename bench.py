@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, published (the fp8 x fp4 scaled MFMA runs at this rate)
 METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
 CSRC = os.path.join(ROOT, "mxfp4_routed_expert_moe_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -43,6 +44,8 @@ def _parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=40,
                    help="tokens of the workload the CPU oracle runs on (about 10-15 s of work)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ffn-split-fp8", action="store_true",
+                   help="prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size first (to scale HBM counters)")
     return p.parse_args()
@@ -132,7 +135,7 @@ def main():
     blob0 = torch.from_numpy(packed).to(dev)
     del packed
     blobs = [blob0] + [blob0.clone() for _ in range(args.copies - 1)]
-    experts = [B.Experts(b, E, H, I) for b in blobs]
+    experts = [B.Experts(b, E, H, I, split_fp8=args.ffn_split_fp8) for b in blobs]
     to_dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     layer = B.MoeLayer(experts[0], T, k, WL.ROUTE_SCALE, WL.CLAMP_LIMIT, w_router=to_dev(inp.router),
                        sel_bias=to_dev(inp.bias), hash_table=to_dev(inp.table))
@@ -186,11 +189,19 @@ def main():
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4))
         traffic = read_traffic(wl.name, "ffn_decode.hip")
-    else:
+    elif not args.ffn_split_fp8:
         achieved = gateup_flops / (gateup_ms * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_MFMA_PEAK_TFLOPS, 4))
         traffic = read_traffic(wl.name, "ffn_prefill.hip")
+    else:
+        # fp8 x fp4 scaled MFMA at its own (fp8) peak; each product is issued
+        # twice (the hi and lo activation terms), and the timed launch pair
+        # includes splitting x.
+        achieved = gateup_flops / (gateup_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), issued_tflops=round(2 * achieved, 1))
+        traffic = read_traffic(wl.name, "ffn_prefill_f8.hip")
     roof["traffic"] = traffic
     roof["kernel"] = "ffn gate/up (moe_expert_ffn phase 1)"
     roof["avg_launch_us"] = round(gateup_ms * 1e3, 2)
@@ -209,12 +220,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8x2-fp4" if (args.ffn_split_fp8 and not decode) else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
                    "routing": wl.routing, "bias": wl.bias, "weights": "mxfp4 e2m1+e8m0/32",
                    "experts_read_per_step": used, "expert_bytes_per_step": layer_bytes,
-                   "blob_copies_rotated": len(experts)},
+                   "blob_copies_rotated": len(experts),
+                   "ffn_prefill_arith": "split-fp8 scaled mfma" if args.ffn_split_fp8 else "bf16 mfma"},
         "roofline": roof,
         "layer_hbm_gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "stages_us": {"ffn_gateup": round(gateup_ms * 1e3, 2), "ffn_down": round(down_ms * 1e3, 2)},

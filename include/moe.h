@@ -48,6 +48,21 @@ extern "C" {
 #define MOE_LAYOUT_CANONICAL_MXFP4 0x4D584330u  /* host reference layout, below */
 #define MOE_LAYOUT_GFX950_TILED_V1 0x4D584731u  /* device layout read by the kernels */
 
+/*
+ * moe_experts.flags.  MOE_FFN_SPLIT_FP8 moves the prefill family of the expert
+ * FFN (the token counts that do not take the decode family) onto the gfx950
+ * scaled matrix cores, which take the E2M1 weights and their E8M0 scales as
+ * stored.  Their other operand must be an 8-bit float, so each bf16
+ * activation a (x, then h) is carried as two E4M3 terms under one E8M0 scale
+ * S per 32 consecutive k:  a = S * hi + (S / 16) * lo.  That is exact for
+ * every value within 2^13 of its block's largest magnitude and off by at
+ * most 2^-21 of that magnitude below it (the reading of "Model techniques map
+ * -- DeepSeek-V4-Flash", row "MXFP4 experts", taken for this option: weights
+ * stay MXFP4, activations keep bf16 precision).  Default 0: the weights are
+ * decoded to bf16 for bf16 matrix cores.  The flag changes the workspace size.
+ */
+#define MOE_FFN_SPLIT_FP8 1
+
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,      /* NULL pointer, negative size, inconsistent arguments */
@@ -97,7 +112,7 @@ typedef struct moe_experts {
   int32_t n_experts;      /* routed experts E (blob holds E + 1 experts) */
   int32_t hidden;         /* H */
   int32_t inter;          /* I */
-  int32_t reserved;       /* must be 0 */
+  int32_t flags;          /* 0, or MOE_FFN_SPLIT_FP8 */
   uint64_t expert_bytes;  /* must equal moe_expert_bytes(H, I) */
   const void* base;       /* device pointer, 256-byte aligned */
 } moe_experts;
@@ -181,8 +196,9 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
  *   h = bf16( silu(min(g, L)) * min(max(u, -L), L) )
  *   out_rows[p] = W_down[e] h                        (float32 accumulation)
  * for each row p of group e, x = x[row_token[p]].  The MXFP4 weights are
- * decoded to bf16 on the fly and fed to bf16 MFMA; only the experts that own
- * rows are read.
+ * decoded to bf16 on the fly and fed to bf16 MFMA (or, with MOE_FFN_SPLIT_FP8
+ * in experts->flags and a prefill-sized T, fed as stored to the scaled FP4
+ * matrix cores); only the experts that own rows are read.
  *
  * x         bf16 [T, H]; experts: descriptor (host pointer) of the device blob
  * offsets, row_token: as written by moe_dispatch for the same T, E, top_k
@@ -198,7 +214,7 @@ int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int
 /*
  * The same expert FFN enqueued one launch at a time, for callers that time or
  * interleave the launches: phase 0 builds the work list from offsets, phase 1
- * runs gate/up + clamped SwiGLU into the workspace (h, bf16), phase 2 runs
+ * runs gate/up + clamped SwiGLU into the workspace (h), phase 2 runs
  * the down projection into out_rows.  Phases 0, 1, 2 issued in order on one
  * stream with identical arguments (same workspace) equal one moe_expert_ffn
  * call bit for bit.  phase -1 runs all three; any other value is MOE_EINVAL.

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_ABI_VERSION = 1
 MOE_LAYOUT_CANONICAL_MXFP4 = 0x4D584330
 MOE_LAYOUT_GFX950_TILED_V1 = 0x4D584731
+MOE_FFN_SPLIT_FP8 = 1  # moe_experts.flags: prefill expert FFN on the scaled FP4 matrix cores
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "MOE_ESHAPE",
           5: "MOE_EWORKSPACE", 6: "MOE_EHIP"}
 
@@ -36,7 +37,7 @@ class MoeError(RuntimeError):
 
 class moe_experts(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("layout", ctypes.c_uint32), ("n_experts", ctypes.c_int32),
-                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("expert_bytes", ctypes.c_uint64), ("base", ctypes.c_void_p)]
 
 
@@ -137,7 +138,7 @@ def _dev(t, dtypes, name):
 class Experts:
     """A device-layout expert blob on the GPU and its C descriptor."""
 
-    def __init__(self, blob_device, n_experts: int, hidden: int, inter: int):
+    def __init__(self, blob_device, n_experts: int, hidden: int, inter: int, split_fp8: bool = False):
         torch = _torch()
         _dev(blob_device, torch.uint8, "blob")
         self.blob = blob_device
@@ -145,12 +146,14 @@ class Experts:
         self.desc = moe_experts()
         _check("moe_experts_init", lib().moe_experts_init(ctypes.byref(self.desc), _ptr(blob_device), n_experts,
                                                           hidden, inter))
+        self.desc.flags = MOE_FFN_SPLIT_FP8 if split_fp8 else 0
 
     @classmethod
-    def from_canonical(cls, canonical: np.ndarray, n_experts: int, hidden: int, inter: int, device="cuda"):
+    def from_canonical(cls, canonical: np.ndarray, n_experts: int, hidden: int, inter: int, device="cuda",
+                       split_fp8: bool = False):
         torch = _torch()
         packed = pack_mxfp4(canonical, n_experts + 1, hidden, inter)
-        return cls(torch.from_numpy(packed).to(device), n_experts, hidden, inter)
+        return cls(torch.from_numpy(packed).to(device), n_experts, hidden, inter, split_fp8)
 
 
 def route(x, T: int, E: int, top_k: int, route_scale: float, w_router=None, sel_bias=None, token_ids=None,

@@ -17,8 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_decode.hip", "ffn_prefill.hip", "combine.hip",
-           "pack.cpp"]
+SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_decode.hip", "ffn_prefill.hip",
+           "ffn_prefill_f8.hip", "combine.hip", "pack.cpp"]
 ARCH = "gfx950"
 
 

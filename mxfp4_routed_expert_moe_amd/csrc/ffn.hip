@@ -33,14 +33,38 @@ inline int ffn_max_items(int T, int E, int k, int bm) {
   return static_cast<int>((rows + bm - 1) / bm) + E + 1;
 }
 
-inline FfnWs ffn_carve(void* ws, int max_items) {
+inline size_t qact_bytes(long rows, int K) {
+  return 2 * align256(static_cast<size_t>(rows) * K) + align256(static_cast<size_t>(rows) * (K / 32));
+}
+
+inline QAct qact_carve(char*& p, long rows, int K) {
+  QAct q;
+  q.hi = reinterpret_cast<uint8_t*>(p);
+  p += align256(static_cast<size_t>(rows) * K);
+  q.lo = reinterpret_cast<uint8_t*>(p);
+  p += align256(static_cast<size_t>(rows) * K);
+  q.sc = reinterpret_cast<uint8_t*>(p);
+  p += align256(static_cast<size_t>(rows) * (K / 32));
+  return q;
+}
+
+// The prefill path (split = true) keeps x and h in split form only; the
+// decode path keeps h as bf16.
+inline FfnWs ffn_carve(void* ws, int max_items, int T, int k, int H, int I, bool split) {
   char* p = static_cast<char*>(ws);
   FfnWs w;
   w.n_items = reinterpret_cast<int32_t*>(p);
   p += 256;
   w.items = reinterpret_cast<int4*>(p);
   p += align256(sizeof(int4) * static_cast<size_t>(max_items));
-  w.h = reinterpret_cast<uint16_t*>(p);
+  w.h = nullptr;
+  w.xq = w.hq = QAct{nullptr, nullptr, nullptr};
+  if (split) {
+    w.xq = qact_carve(p, T, H);
+    w.hq = qact_carve(p, static_cast<long>(T) * (k + 1), I);
+  } else {
+    w.h = reinterpret_cast<uint16_t*>(p);
+  }
   return w;
 }
 
@@ -75,19 +99,21 @@ inline int ffn_bm(int T, int E, int k, int H, int I) { return use_decode(T, E, k
 
 }  // namespace
 
-size_t ffn_ws_bytes(int T, int E, int H, int I, int k) {
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8) {
   const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I));
-  return 256 + align256(sizeof(int4) * static_cast<size_t>(mi)) +
-         align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
+  const size_t n = 256 + align256(sizeof(int4) * static_cast<size_t>(mi));
+  if (split_fp8 && !use_decode(T, E, k, H, I)) return n + qact_bytes(T, H) + qact_bytes(static_cast<long>(T) * (k + 1), I);
+  return n + align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
 }
 
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, hipStream_t s) {
+                      void* ws, int phase, bool split_fp8, hipStream_t s) {
   const int bm = ffn_bm(T, E, k, H, I);
   const int max_items = ffn_max_items(T, E, k, bm);
   const bool dec = use_decode(T, E, k, H, I);
-  FfnWs w = ffn_carve(ws, max_items);
+  const bool split = split_fp8 && !dec;
+  FfnWs w = ffn_carve(ws, max_items, T, k, H, I, split);
   for (int ph = 0; ph < 3; ++ph) {
     if (phase >= 0 && ph != phase) continue;
     if (ph == 0) {
@@ -97,8 +123,16 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
       const bool gateup = ph == 1;
       const uint16_t* act = gateup ? x : w.h;
       const int32_t* rt = gateup ? row_token : nullptr;
-      if (dec) launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, s);
-      else launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+      if (dec) {
+        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, s);
+      } else if (split) {
+        // phase 1 splits x, then writes h split; phase 2 reads it
+        if (gateup) launch_quant_act(x, T, H, w.xq, s);
+        launch_ffn_prefill_f8(gateup, gateup ? w.xq : w.hq, rt, w, blob, expert_bytes, H, I, limit, out_rows,
+                              max_items, s);
+      } else {
+        launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+      }
     }
   }
   return hipGetLastError();

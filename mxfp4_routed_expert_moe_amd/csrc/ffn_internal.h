@@ -6,11 +6,22 @@
 
 namespace moe {
 
-// Device-side work list and the h buffer, carved from the FFN workspace.
+// Activations as two scaled E4M3 terms: v = S * hi + (S / 16) * lo, with one
+// E8M0 scale byte sc (S = 2^(sc - 127)) per 32 consecutive k of a row.
+struct QAct {
+  uint8_t* hi;  // [rows, K]
+  uint8_t* lo;  // [rows, K]
+  uint8_t* sc;  // [rows, K / 32]
+};
+
+// Device-side work list, the h buffer and the prefill split activations,
+// carved from the FFN workspace.
 struct FfnWs {
   int32_t* n_items;  // [1]
   int4* items;       // [max_items] (group, first row, row count, 0)
   uint16_t* h;       // [rows, I] bf16
+  QAct xq;           // [T, H] (prefill)
+  QAct hq;           // [rows, I] (prefill)
 };
 
 constexpr int kDecodeRows = 16;    // rows per decode item
@@ -29,5 +40,9 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
                         hipStream_t s);
+void launch_quant_act(const uint16_t* src, int rows, int K, const QAct& dst, hipStream_t s);
+void launch_ffn_prefill_f8(bool gateup, const QAct& aq, const int32_t* row_token, const FfnWs& w,
+                           const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows,
+                           int max_items, hipStream_t s);
 
 }  // namespace moe

@@ -21,7 +21,7 @@ int check_experts(const moe_experts* d) {
   if (!d || !d->base) return MOE_EINVAL;
   if (d->abi_version != MOE_ABI_VERSION) return MOE_ELAYOUT;
   if (d->layout != MOE_LAYOUT_GFX950_TILED_V1) return MOE_ELAYOUT;
-  if (d->reserved != 0) return MOE_EINVAL;
+  if ((d->flags & ~MOE_FFN_SPLIT_FP8) != 0) return MOE_EINVAL;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_ESHAPE;
   const uint64_t eb = moe_expert_bytes(d->hidden, d->inter);
   if (eb == 0 || d->expert_bytes != eb) return MOE_ESHAPE;
@@ -57,7 +57,7 @@ int moe_experts_init(moe_experts* d, const void* base, int32_t n_experts, int32_
   d->n_experts = n_experts;
   d->hidden = hidden;
   d->inter = inter;
-  d->reserved = 0;
+  d->flags = 0;
   d->expert_bytes = eb;
   d->base = base;
   return MOE_OK;
@@ -109,7 +109,8 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
 
 size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k) {
   if (T <= 0 || top_k < 1 || top_k > kMaxTopK || check_experts(experts) != MOE_OK) return 0;
-  return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k);
+  return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k,
+                           (experts->flags & MOE_FFN_SPLIT_FP8) != 0);
 }
 
 namespace {
@@ -129,7 +130,8 @@ int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t t
   if (ws_bytes < moe_ffn_workspace_size(T, experts, top_k)) return MOE_EWORKSPACE;
   return hip_status(moe::launch_ffn(x, T, static_cast<const uint8_t*>(experts->base), experts->expert_bytes,
                                     experts->n_experts, experts->hidden, experts->inter, top_k, offsets, row_token,
-                                    clamp_limit, out_rows, ws, phase, as_stream(stream)));
+                                    clamp_limit, out_rows, ws, phase, (experts->flags & MOE_FFN_SPLIT_FP8) != 0,
+                                    as_stream(stream)));
 }
 
 }  // namespace

@@ -159,10 +159,11 @@ size_t dispatch_ws_bytes(int T, int E, int k);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t s);
 
-size_t ffn_ws_bytes(int T, int E, int H, int I, int k);
+// split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8).
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8);
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, hipStream_t s);
+                      void* ws, int phase, bool split_fp8, hipStream_t s);
 
 hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s);

@@ -178,7 +178,7 @@ def test_ffn_checks():
     assert _ffn(d=_desc(expert_bytes=13_369_344 + 32)) == ESHAPE
     assert _ffn(d=_desc(hidden=4000)) == ESHAPE
     assert _ffn(d=_desc(n_experts=0)) == ESHAPE
-    assert _ffn(d=_desc(reserved=1)) == EINVAL
+    assert _ffn(d=_desc(flags=2)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
     assert _ffn(d=_desc(base=FAKE + 128)) == EALIGN
     assert _ffn(d=_desc(base=None)) == EINVAL
     assert _ffn(k=0) == ESHAPE and _ffn(k=9) == ESHAPE
@@ -188,6 +188,15 @@ def test_ffn_checks():
     assert _ffn(x=FAKE_MIS) == EALIGN and _ffn(out=FAKE_MIS) == EALIGN and _ffn(ws=FAKE + 64) == EALIGN
     need = B.lib().moe_ffn_workspace_size(64, ctypes.byref(_desc()), 6)
     assert need > 64 * 7 * 2048 * 2 and _ffn(ws_bytes=need - 1) == EWORKSPACE
+    # MOE_FFN_SPLIT_FP8 changes only the prefill family's workspace: x and h
+    # as two byte planes plus one scale byte per 32 (no bf16 h)
+    split = _desc(flags=B.MOE_FFN_SPLIT_FP8)
+    assert B.lib().moe_ffn_workspace_size(64, ctypes.byref(split), 6) == need
+    T = 4096
+    plain = B.lib().moe_ffn_workspace_size(T, ctypes.byref(_desc()), 6)
+    two = B.lib().moe_ffn_workspace_size(T, ctypes.byref(split), 6)
+    planes = lambda rows, K: 2 * rows * K + rows * K // 32  # noqa: E731
+    assert two - plain == planes(T, 4096) + planes(7 * T, 2048) - 7 * T * 2048 * 2
     assert B.lib().moe_ffn_workspace_size(64, ctypes.byref(_desc(layout=1)), 6) == 0
 
 

@@ -141,8 +141,8 @@ def _identity_blob(hidden, inter, n_total, up_code):
     return blob
 
 
-@pytest.mark.parametrize("T", [4, 300])
-def test_identity_experts_closed_form_and_orientation(T):
+@pytest.mark.parametrize("T,split", [(4, False), (300, False), (300, True)])
+def test_identity_experts_closed_form_and_orientation(T, split):
     # gate = I, up = 2I, down = I: every expert row is silu(min(x,L)) * clamp(2x,-L,L)
     # in its first I columns and 0 beyond; a swapped gate/up would differ.
     H, I, E, L = 1024, 512, 16, WL.CLAMP_LIMIT
@@ -152,13 +152,22 @@ def test_identity_experts_closed_form_and_orientation(T):
     inp.x = WL.f32_to_bf16_bits(xf)
     blob = _identity_blob(H, I, E + 1, 0x4)
     inp.experts = blob
-    g = LC.run_gpu_layer(inp, B.Experts.from_canonical(blob, E, H, I))
+    g = LC.run_gpu_layer(inp, B.Experts.from_canonical(blob, E, H, I, split_fp8=split))
     rows = LC.host(g["out_rows"][: int(g["offsets"][-1])]).astype(np.float64)
     v = O.bf16_bits_to_f64(inp.x)[g["row_token"][: rows.shape[0]], :I]
     silu = lambda a: a / (1 + np.exp(-a))  # noqa: E731
     want = silu(np.minimum(v, L)) * np.clip(2 * v, -L, L)
-    # h is rounded to bf16 (half an ulp: 2^-8 relative); the fp32 SiLU adds ~1e-6
-    assert np.all(np.abs(rows[:, :I] - want) <= 2.0 ** -8 * (1 + 1e-4) * np.abs(want) + 1e-30)
+    # h is rounded to bf16 (half an ulp: 2^-8 relative); the fp32 SiLU adds ~1e-6.
+    tol = 2.0 ** -8 * (1 + 1e-4) * np.abs(want) + 1e-30
+    if split:
+        # Two E4M3 terms under one power-of-two scale per 32 k are exact down
+        # to 2^-13 of the block's largest magnitude and off by at most 2^-21
+        # of it below that.  For x this moves only |v| < 2^-13 max|x|, where
+        # the SwiGLU slope is about 2|v|; for h it lands on the output as is:
+        # allow 2^-18 of the 32-column block maximum.
+        blk = np.repeat(np.abs(want).reshape(want.shape[0], I // 32, 32).max(axis=2), 32, axis=1)
+        tol = tol + 2.0 ** -18 * blk
+    assert np.all(np.abs(rows[:, :I] - want) <= tol)
     assert np.all(rows[:, I:] == 0)
     swapped = silu(np.minimum(2 * v, L)) * np.clip(v, -L, L)
     assert np.mean(np.abs(rows[:, :I] - swapped)) > 0.1
@@ -353,5 +362,44 @@ def test_full_workloads(index, sample):
         counts = np.diff(r["g"]["offsets"][: WL.N_EXPERTS + 1])
         assert counts.max() >= 0.98 * w.T              # the hottest expert takes nearly every token
         assert np.median(counts) < 200
+    del r
+    torch.cuda.empty_cache()
+
+
+# The prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8).
+@pytest.mark.parametrize("T,H,I,E", [(300, 512, 512, 16), (700, 512, 512, 256), (200, 1024, 2048, 32)])
+def test_split_fp8_small_shapes(T, H, I, E):
+    print(f"[parity] split fp8 T={T} H={H} I={I} E={E}", flush=True)
+    inp = _small_inputs(T, H, I, E, 1000 + T)
+    ex = B.Experts.from_canonical(inp.experts, E, H, I, split_fp8=True)
+    r = LC.full_check(inp, ex)
+    assert r["ambiguous"] == 0
+    g = r["g"]
+    ref = O.moe_layer(inp.x, inp.experts, n_experts=E, hidden=H, inter=I, top_k=6, route_scale=1.5,
+                      limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table)
+    assert np.array_equal(g["offsets"], ref["offsets"])
+    n = int(ref["offsets"][-1])
+    LC.assert_output_close(LC.host(g["out_rows"][:n]), ref["out_rows"], "all rows")
+    LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
+
+
+def test_split_fp8_leaves_decode_unchanged():
+    # the flag moves only the prefill family: decode-sized calls are bit-identical
+    inp = _small_inputs(6, 1024, 512, 32, 77)
+    a = LC.run_gpu_layer(inp, _experts(inp))
+    b = LC.run_gpu_layer(inp, B.Experts.from_canonical(inp.experts, 32, 1024, 512, split_fp8=True))
+    n = int(a["offsets"][-1])
+    assert torch.equal(a["out_rows"][:n], b["out_rows"][:n])
+
+
+@pytest.mark.parametrize("index,sample", [(3, 8), (4, 8)])
+def test_split_fp8_full_prefill_workloads(index, sample):
+    w = WL.WORKLOADS[index]
+    print(f"[parity] split fp8 full workload {w.name} T={w.T}", flush=True)
+    inp, _ = _full_inputs(index)
+    ex = B.Experts(_full_inputs(index)[1].blob, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, split_fp8=True)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index)
+    print(f"[parity] split fp8 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r
     torch.cuda.empty_cache()

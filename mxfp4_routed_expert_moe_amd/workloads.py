@@ -145,6 +145,39 @@ def make_experts(seed: int, n_total: int, hidden: int = HIDDEN, inter: int = INT
     return out
 
 
+def mxfp8_expert_bytes(hidden: int, inter: int) -> int:
+    """Bytes of one MXFP8 expert: three projections of one E4M3 byte per weight
+    plus one E8M0 byte per 32 weights."""
+    return 3 * hidden * inter + 3 * hidden * inter // 32
+
+
+def make_shared_mxfp8(seed: int, hidden: int = HIDDEN, inter: int = INTER, scale_lo: int = 113,
+                      scale_hi: int = 117) -> np.ndarray:
+    """Canonical MXFP8 shared expert, uint8: per projection (gate [I,H], up [I,H],
+    down [H,I]) the row-major E4M3 codes, then the [n, k/32] E8M0 scales.
+
+    Codes are uniform over the 254 finite E4M3 codes (0x7f and 0xff, the NaN
+    codes, are skipped) and scale bytes uniform over [scale_lo, scale_hi], i.e.
+    2^U{-14..-10} by default, which puts the weights at about the magnitude of
+    the MXFP4 experts (mean |code value| ~44 against ~2.25 for E2M1)."""
+    g = _rng(seed, 4, 0)
+    out = np.empty(mxfp8_expert_bytes(hidden, inter), dtype=np.uint8)
+    pos = 0
+    for n, k in ((inter, hidden), (inter, hidden), (hidden, inter)):
+        r = g.integers(0, 254, size=n * k, dtype=np.int32)
+        out[pos:pos + n * k] = (r + (r >= 0x7f) + (r >= 0xfe)).astype(np.uint8)
+        pos += n * k
+        out[pos:pos + n * k // 32] = g.integers(scale_lo, scale_hi + 1, size=n * k // 32, dtype=np.uint8)
+        pos += n * k // 32
+    return out
+
+
+def make_experts_shared_mxfp8(seed: int, n_experts: int, hidden: int = HIDDEN, inter: int = INTER) -> np.ndarray:
+    """Canonical blob: n_experts MXFP4 routed experts (as make_experts) followed
+    by the MXFP8 shared expert (make_shared_mxfp8)."""
+    return np.concatenate([make_experts(seed, n_experts, hidden, inter), make_shared_mxfp8(seed, hidden, inter)])
+
+
 def make_hash(seed: int, T: int, n_experts: int = N_EXPERTS, top_k: int = TOP_K,
               vocab: int = HASH_VOCAB):
     """Token ids uniform over [0, vocab) and a table [vocab, top_k] int32 whose

@@ -27,6 +27,9 @@ What the layer computes, with the passage each step follows:
   Sizes: E2M1 codes with one E8M0 scale per group of 32 columns).
 * Shared expert and combine (techniques map, row "Shared expert"): the routed
   outputs weighted and summed, plus the shared expert applied to the same input.
+* Optionally the shared expert in MXFP8 ("ElytronAI / DeepSeek-v4-Flash",
+  Sizes: the dense weights as E4M3 with one E8M0 scale per 32 columns, the
+  mxfp8_lt re-encode), otherwise in MXFP4 like the routed experts.
 
 Readings where the pages are silent (each also listed with the design notes):
 E2M1/E8M0 bit meaning per the OCP microscaling formats; low nibble = even
@@ -51,6 +54,27 @@ import numpy as np
 # Codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6; codes 8..15 are their negatives.
 E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
                         -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0], dtype=np.float64)
+
+
+def _e4m3_table() -> np.ndarray:
+    """E4M3 code -> value (OCP FP8 E4M3, the variant without infinities):
+    sign bit 7, exponent bits 6:3 with bias 7, mantissa bits 2:0.  Exponent 0
+    is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448."""
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 0xF and m == 0x7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3_VALUES = _e4m3_table()
 
 
 def e8m0_value(e) -> np.ndarray:
@@ -103,21 +127,47 @@ def decode_mxfp4(nibbles: np.ndarray, scales: np.ndarray, n_out: int, k_in: int)
     return w.reshape(n_out, k_in)
 
 
+def decode_mxfp8(codes: np.ndarray, scales: np.ndarray, n_out: int, k_in: int) -> np.ndarray:
+    """Decode one canonical MXFP8 projection to float64 [n_out, k_in]:
+    W[r, c] = E4M3(code[r, c]) * 2^(scale[r, c // 32] - 127), one code byte
+    per weight in row-major order, then the [n_out, k_in / 32] scale bytes."""
+    cd = np.asarray(codes, dtype=np.uint8).reshape(n_out, k_in)
+    sc = np.asarray(scales, dtype=np.uint8).reshape(n_out, k_in // 32)
+    w = E4M3_VALUES[cd].reshape(n_out, k_in // 32, 32)
+    w *= e8m0_value(sc)[:, :, None]
+    return w.reshape(n_out, k_in)
+
+
 def canonical_expert_size(hidden: int, inter: int) -> int:
     """Bytes of one canonical expert (gate, up, down; 4.25 bits per weight)."""
     proj = lambda n, k: n * k // 2 + n * k // 32  # noqa: E731
     return 2 * proj(inter, hidden) + proj(hidden, inter)
 
 
-def decode_expert(blob: np.ndarray, xid: int, hidden: int, inter: int):
-    """Decode expert xid of a canonical blob -> (gate [I,H], up [I,H], down [H,I])."""
+def canonical_mxfp8_expert_size(hidden: int, inter: int) -> int:
+    """Bytes of one canonical MXFP8 expert (gate, up, down; 8.25 bits per weight)."""
+    proj = lambda n, k: n * k + n * k // 32  # noqa: E731
+    return 2 * proj(inter, hidden) + proj(hidden, inter)
+
+
+def decode_expert(blob: np.ndarray, xid: int, hidden: int, inter: int, fmt: str = "mxfp4"):
+    """Decode expert xid of a canonical blob -> (gate [I,H], up [I,H], down [H,I]).
+
+    The blob holds MXFP4 experts back to back; fmt = "mxfp8" reads an MXFP8
+    expert starting where MXFP4 expert xid would (the shared expert stored
+    last, after the routed ones)."""
     eb = canonical_expert_size(hidden, inter)
-    base = xid * eb
+    pos = xid * eb
     mats = []
-    pos = base
     for n, k in ((inter, hidden), (inter, hidden), (hidden, inter)):
-        nn, ns = n * k // 2, n * k // 32
-        mats.append(decode_mxfp4(blob[pos:pos + nn], blob[pos + nn:pos + nn + ns], n, k))
+        if fmt == "mxfp4":
+            nn, ns = n * k // 2, n * k // 32
+            mats.append(decode_mxfp4(blob[pos:pos + nn], blob[pos + nn:pos + nn + ns], n, k))
+        elif fmt == "mxfp8":
+            nn, ns = n * k, n * k // 32
+            mats.append(decode_mxfp8(blob[pos:pos + nn], blob[pos + nn:pos + nn + ns], n, k))
+        else:
+            raise ValueError(f"unknown weight format {fmt!r}")
         pos += nn + ns
     return tuple(mats)
 
@@ -229,11 +279,12 @@ def expert_forward(xf: np.ndarray, mats, limit: float) -> np.ndarray:
 
 
 def expert_ffn(x_bits, blob, offsets, row_token, limit: float, n_experts: int, hidden: int, inter: int,
-               groups=None) -> np.ndarray:
+               groups=None, shared_fmt: str = "mxfp4") -> np.ndarray:
     """Every dispatched row through its expert -> float64 [rows, H].
 
     Expert-major: each group with rows is decoded once, then its rows run.
-    `groups` optionally restricts the work to some groups (other rows stay 0).
+    `groups` optionally restricts the work to some groups (other rows stay 0);
+    shared_fmt is the weight format of the shared expert (group n_experts).
     """
     xf = bf16_bits_to_f64(x_bits)
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -243,7 +294,7 @@ def expert_ffn(x_bits, blob, offsets, row_token, limit: float, n_experts: int, h
         r0, r1 = int(offsets[g]), int(offsets[g + 1])
         if r1 == r0:
             continue
-        mats = decode_expert(blob, g, hidden, inter)
+        mats = decode_expert(blob, g, hidden, inter, shared_fmt if g == n_experts else "mxfp4")
         out[r0:r1] = expert_forward(xf[row_token[r0:r1]], mats, limit)
     return out
 
@@ -266,7 +317,8 @@ def combine(out_rows: np.ndarray, slot_row: np.ndarray, weights: np.ndarray) -> 
 
 
 def moe_layer(x_bits, blob, *, n_experts: int, hidden: int, inter: int, top_k: int,
-              route_scale: float, limit: float, w_router=None, bias=None, token_ids=None, table=None):
+              route_scale: float, limit: float, w_router=None, bias=None, token_ids=None, table=None,
+              shared_fmt: str = "mxfp4"):
     """The whole layer: route -> dispatch -> expert FFN -> combine.  Returns a dict
     with ids, weights, offsets, row_token, slot_row, out_rows and y (float64)."""
     if table is not None:
@@ -274,13 +326,14 @@ def moe_layer(x_bits, blob, *, n_experts: int, hidden: int, inter: int, top_k: i
     else:
         ids, w, _ = route_learned(x_bits, w_router, bias, top_k, route_scale)
     offsets, row_token, slot_row = dispatch(ids, n_experts)
-    out = expert_ffn(x_bits, blob, offsets, row_token, limit, n_experts, hidden, inter)
+    out = expert_ffn(x_bits, blob, offsets, row_token, limit, n_experts, hidden, inter, shared_fmt=shared_fmt)
     y = combine(out, slot_row, w)
     return dict(ids=ids, weights=w, offsets=offsets, row_token=row_token, slot_row=slot_row,
                 out_rows=out, y=y)
 
 
-def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, inter: int, limit: float):
+def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, inter: int, limit: float,
+                    shared_fmt: str = "mxfp4"):
     """Brute force without dispatch: every token through ALL experts, masked by a
     0/1 selection mask and weighted, plus the shared expert.  Tiny inputs only."""
     xf = bf16_bits_to_f64(x_bits)
@@ -293,5 +346,5 @@ def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, 
         sel = mask.any(axis=1).astype(np.float64)
         ye = expert_forward(xf, decode_expert(blob, e, hidden, inter), limit)
         y += (sel * we)[:, None] * ye
-    y += expert_forward(xf, decode_expert(blob, n_experts, hidden, inter), limit)
+    y += expert_forward(xf, decode_expert(blob, n_experts, hidden, inter, shared_fmt), limit)
     return y

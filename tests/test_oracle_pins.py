@@ -403,3 +403,93 @@ def test_combine_weights_and_shared_term():
                 want += w[t, j] * out[slot_row[t, j]]
         want += out[18 + t]               # routed sum first, then the shared expert
         assert np.array_equal(y[t], want)
+
+
+# ---------------------------------------------------------------- MXFP8 shared expert
+def test_e4m3_table_matches_torch_float8():
+    # torch's float8_e4m3fn is an independent implementation of the same OCP format
+    t = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(O.E4M3_VALUES), np.isnan(t))
+    ok = ~np.isnan(t)
+    assert np.array_equal(O.E4M3_VALUES[ok], t[ok])
+    assert np.array_equal(np.signbit(O.E4M3_VALUES[ok]), np.signbit(t[ok]))
+
+
+def test_e4m3_closed_forms():
+    v = O.E4M3_VALUES
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0          # 1.75 * 2^8, the largest finite
+    assert v[0x38] == 1.0 and v[0xB8] == -1.0               # exponent field 7 = bias
+    assert v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9    # smallest normal, smallest subnormal
+    assert v[0x07] == 7 * 2.0 ** -9                          # largest subnormal
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isnan(v).sum() == 2
+    assert v[0x00] == 0.0 and v[0x80] == 0.0 and np.signbit(v[0x80])
+
+
+def test_decode_mxfp8_matches_torch_and_scale_axis():
+    rng = np.random.default_rng(8)
+    n, k = 5, 96
+    codes = rng.integers(0, 256, size=(n, k), dtype=np.int32).astype(np.uint8)
+    codes[codes == 0x7F] = 0x00
+    codes[codes == 0xFF] = 0x80
+    scales = rng.integers(110, 135, size=(n, k // 32), dtype=np.int32).astype(np.uint8)
+    w = O.decode_mxfp8(codes.ravel(), scales.ravel(), n, k)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).double()
+    s = torch.from_numpy(scales.astype(np.float64) - 127.0)
+    want = (t * torch.pow(2.0, s).repeat_interleave(32, dim=1)).numpy()
+    assert np.array_equal(w, want)
+
+
+def _mxfp8_copy_of_shared(blob, E, hidden, inter):
+    """The blob with its MXFP4 shared expert re-encoded as MXFP8: each E2M1
+    value is an E4M3 value too (encoded by torch), with the same scales."""
+    eb = WL.expert_bytes(hidden, inter)
+    off = WL.expert_plane_offsets(hidden, inter)
+    base = E * eb
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    to_e4m3 = e2m1.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    parts = []
+    for name, n, k in (("gate", inter, hidden), ("up", inter, hidden), ("down", hidden, inter)):
+        nib = blob[base + off[name + "_nib"]: base + off[name + "_nib"] + n * k // 2].reshape(n, k // 2)
+        codes = np.empty((n, k), dtype=np.uint8)
+        codes[:, 0::2] = to_e4m3[nib & 0x0F]      # low nibble = even column
+        codes[:, 1::2] = to_e4m3[nib >> 4]
+        parts += [codes.ravel(), blob[base + off[name + "_sc"]: base + off[name + "_sc"] + n * k // 32]]
+    return np.concatenate([blob[:base]] + parts)
+
+
+def test_mxfp8_shared_equals_its_mxfp4_original():
+    # the MXFP8 reader (its own layout code) must give the layer exactly what
+    # the MXFP4 reader gives for the same weights
+    T, hidden, inter, E = 9, 64, 64, 16
+    x, blob, kw, rk = _tiny_layer(T, hidden, inter, E, 41)
+    b8 = _mxfp8_copy_of_shared(blob, E, hidden, inter)
+    assert len(b8) == E * WL.expert_bytes(hidden, inter) + WL.mxfp8_expert_bytes(hidden, inter)
+    assert len(b8) - E * O.canonical_expert_size(hidden, inter) == O.canonical_mxfp8_expert_size(hidden, inter)
+    r4 = O.moe_layer(x, blob, **kw, **rk)
+    r8 = O.moe_layer(x, b8, **kw, **rk, shared_fmt="mxfp8")
+    assert np.array_equal(r4["out_rows"], r8["out_rows"]) and np.array_equal(r4["y"], r8["y"])
+
+
+@pytest.mark.parametrize("routing", ["learned", "hash"])
+def test_dense_brute_force_equals_sparse_mxfp8_shared(routing):
+    T, hidden, inter, E = 8, 64, 32, 16
+    x, _, kw, rk = _tiny_layer(T, hidden, inter, E, 23, routing)
+    blob = WL.make_experts_shared_mxfp8(23, E, hidden, inter)
+    r = O.moe_layer(x, blob, **kw, **rk, shared_fmt="mxfp8")
+    yd = O.dense_moe_layer(x, blob, r["ids"], r["weights"], n_experts=E, hidden=hidden, inter=inter, limit=10.0,
+                           shared_fmt="mxfp8")
+    assert np.max(np.abs(yd - r["y"])) <= 1e-12 * np.max(np.abs(yd))
+    # the format matters: the same bytes read as an MXFP4 shared expert give another y
+    r4 = O.moe_layer(x, blob, **kw, **rk)
+    assert np.all(np.isfinite(r["y"])) and not np.allclose(r4["y"], r["y"])
+
+
+def test_mxfp8_workload_codes_and_scales():
+    b = WL.make_shared_mxfp8(3, 512, 512)
+    n = 512 * 512
+    codes = np.concatenate([b[0:n], b[n + n // 32: 2 * n + n // 32], b[2 * (n + n // 32): 3 * n + 2 * n // 32]])
+    assert not np.any((codes == 0x7F) | (codes == 0xFF))           # no NaN codes
+    counts = np.bincount(codes, minlength=256)
+    assert counts.min() > 0 or set(np.flatnonzero(counts == 0)) == {0x7F, 0xFF}
+    sc = b[n: n + n // 32]
+    assert sc.min() == 113 and sc.max() == 117

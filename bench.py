@@ -46,6 +46,7 @@ def _parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ffn-split-fp8", action="store_true",
                    help="prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8)")
+    p.add_argument("--shared-mxfp8", action="store_true", help="the shared expert in MXFP8 (MOE_SHARED_MXFP8)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size first (to scale HBM counters)")
     return p.parse_args()
@@ -77,7 +78,7 @@ def read_traffic(workload: str, source: str):
         return None
 
 
-def cpu_baseline(inp, n_tokens: int):
+def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4"):
     """The oracle as it stands, on the first n_tokens of the workload."""
     import numpy as np
     from oracle import moe_oracle as O
@@ -91,7 +92,8 @@ def cpu_baseline(inp, n_tokens: int):
     t0 = time.perf_counter()
     r = O.moe_layer(inp.x[:S], inp.experts, n_experts=inp.n_experts, hidden=inp.hidden, inter=inp.inter,
                     top_k=inp.top_k, route_scale=WL.ROUTE_SCALE, limit=WL.CLAMP_LIMIT, w_router=inp.router,
-                    bias=inp.bias, token_ids=None if inp.tok is None else inp.tok[:S], table=inp.table)
+                    bias=inp.bias, token_ids=None if inp.tok is None else inp.tok[:S], table=inp.table,
+                    shared_fmt=shared_fmt)
     dt = time.perf_counter() - t0
     n_exp = int(np.count_nonzero(np.diff(r["offsets"])))
     return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle",
@@ -117,7 +119,11 @@ def main():
     B.lib()  # fail loudly if the library is missing
     wl = {w.name: w for w in WL.WORKLOADS}[args.workload]
     print(f"[bench] workload {wl.name} T={wl.T}: generating inputs", file=sys.stderr, flush=True)
-    inp = WL.make_layer_inputs(wl)
+    if args.shared_mxfp8 and args.ffn_split_fp8:
+        print("--shared-mxfp8 and --ffn-split-fp8 do not combine", file=sys.stderr)
+        sys.exit(2)
+    inp = WL.make_layer_inputs(wl, experts=WL.make_experts_shared_mxfp8(wl.seed, WL.N_EXPERTS)
+                               if args.shared_mxfp8 else None)
     H, I, E, k, T = inp.hidden, inp.inter, inp.n_experts, inp.top_k, wl.T
 
     dev = torch.device("cuda", 0)
@@ -131,11 +137,15 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    packed = B.pack_mxfp4(inp.experts, E + 1, H, I)
+    if args.shared_mxfp8:
+        nb = E * WL.expert_bytes(H, I)
+        packed = np.concatenate([B.pack_mxfp4(inp.experts[:nb], E, H, I), B.pack_mxfp8(inp.experts[nb:], H, I)])
+    else:
+        packed = B.pack_mxfp4(inp.experts, E + 1, H, I)
     blob0 = torch.from_numpy(packed).to(dev)
     del packed
     blobs = [blob0] + [blob0.clone() for _ in range(args.copies - 1)]
-    experts = [B.Experts(b, E, H, I, split_fp8=args.ffn_split_fp8) for b in blobs]
+    experts = [B.Experts(b, E, H, I, split_fp8=args.ffn_split_fp8, shared_mxfp8=args.shared_mxfp8) for b in blobs]
     to_dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     layer = B.MoeLayer(experts[0], T, k, WL.ROUTE_SCALE, WL.CLAMP_LIMIT, w_router=to_dev(inp.router),
                        sel_bias=to_dev(inp.bias), hash_table=to_dev(inp.table))
@@ -181,7 +191,8 @@ def main():
     used = int(len(np.unique(ids[(ids >= 0) & (ids < E)]))) + 1   # + the shared expert
     rows = int(layer.offsets[-1].item())
     proj_bytes = H * I * 17 // 32
-    gateup_bytes = used * 2 * proj_bytes + rows * H * 2 + rows * I * 2
+    shared_proj = H * I * 33 // 32 if args.shared_mxfp8 else proj_bytes  # the shared expert's projection bytes
+    gateup_bytes = (used - 1) * 2 * proj_bytes + 2 * shared_proj + rows * H * 2 + rows * I * 2
     gateup_flops = rows * 2 * 2 * H * I
     decode = rows <= 16 * (E + 1)
     if decode:
@@ -208,7 +219,7 @@ def main():
     roof["algorithmic_bytes_per_launch"] = gateup_bytes
     roof["algorithmic_flops_per_launch"] = gateup_flops
 
-    layer_bytes = used * 3 * proj_bytes
+    layer_bytes = (used - 1) * 3 * proj_bytes + 3 * shared_proj
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -226,7 +237,8 @@ def main():
                    "routing": wl.routing, "bias": wl.bias, "weights": "mxfp4 e2m1+e8m0/32",
                    "experts_read_per_step": used, "expert_bytes_per_step": layer_bytes,
                    "blob_copies_rotated": len(experts),
-                   "ffn_prefill_arith": "split-fp8 scaled mfma" if args.ffn_split_fp8 else "bf16 mfma"},
+                   "ffn_prefill_arith": "split-fp8 scaled mfma" if args.ffn_split_fp8 else "bf16 mfma",
+                   "shared_expert": "mxfp8" if args.shared_mxfp8 else "mxfp4"},
         "roofline": roof,
         "layer_hbm_gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "stages_us": {"ffn_gateup": round(gateup_ms * 1e3, 2), "ffn_down": round(down_ms * 1e3, 2)},
@@ -234,7 +246,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens, "mxfp8" if args.shared_mxfp8 else "mxfp4")
     print(json.dumps(out), flush=True)
 
 

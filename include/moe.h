@@ -63,6 +63,19 @@ extern "C" {
  */
 #define MOE_FFN_SPLIT_FP8 1
 
+/*
+ * moe_experts.flags.  MOE_SHARED_MXFP8: the shared expert (slot n_experts,
+ * still at base + n_experts * expert_bytes) is MXFP8 -- one E4M3 code per
+ * weight (OCP FP8 without infinities: sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; codes 0x7f and 0xff are NaN) times the same E8M0 group-32
+ * scales -- and takes moe_expert_bytes_mxfp8(H, I) bytes.  This is the
+ * dense-weight format of "ElytronAI / DeepSeek-v4-Flash", Sizes (mxfp8_lt:
+ * one E8M0 per 32 columns), read here as the shared expert's precision, an
+ * inference the pages leave open.  Not combinable with MOE_FFN_SPLIT_FP8
+ * (MOE_EINVAL).
+ */
+#define MOE_SHARED_MXFP8 2
+
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,      /* NULL pointer, negative size, inconsistent arguments */
@@ -105,6 +118,14 @@ uint32_t moe_abi_version(void);
  *     16*(k/512) + 4*i + (l/16).
  * One 64-lane wave reads a tile with one coalesced 16-byte load per lane and
  * holds exactly the 32 codes, and the one scale, that its MFMA fragments need.
+ *
+ * An MXFP8 expert (MOE_SHARED_MXFP8) has the same three projections, each its
+ * code plane uint8 [N][K] (one E4M3 byte per weight, row-major) followed by
+ * its scale plane uint8 [N][K/32], canonically; in the device layout the code
+ * plane is cut into 2048-byte tiles t = (n/16) * (K/128) + (k/128), and inside
+ * a tile lane l = 16*g + r owns bytes [16l, 16l+16) (columns 128*(k/128) +
+ * 32*g .. +15 of row 16*(n/16) + r) and bytes [1024 + 16l, 1024 + 16l + 16)
+ * (columns +16 .. +31); the scale plane is tiled exactly as above.
  */
 typedef struct moe_experts {
   uint32_t abi_version;   /* MOE_ABI_VERSION */
@@ -112,7 +133,7 @@ typedef struct moe_experts {
   int32_t n_experts;      /* routed experts E (blob holds E + 1 experts) */
   int32_t hidden;         /* H */
   int32_t inter;          /* I */
-  int32_t flags;          /* 0, or MOE_FFN_SPLIT_FP8 */
+  int32_t flags;          /* 0, MOE_FFN_SPLIT_FP8 or MOE_SHARED_MXFP8 */
   uint64_t expert_bytes;  /* must equal moe_expert_bytes(H, I) */
   const void* base;       /* device pointer, 256-byte aligned */
 } moe_experts;
@@ -138,6 +159,21 @@ int moe_pack_mxfp4(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_t
                    int32_t inter, uint8_t* dst_device_layout, uint64_t dst_bytes);
 int moe_unpack_mxfp4(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_total, int32_t hidden,
                      int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes);
+
+/* Bytes of one MXFP8 expert of shape (H, I): 3*H*I*33/32; 0 for unsupported shapes. */
+uint64_t moe_expert_bytes_mxfp8(int32_t hidden, int32_t inter);
+
+/*
+ * The same repack for ONE MXFP8 expert (the MOE_SHARED_MXFP8 shared expert):
+ * src and dst are HOST pointers to moe_expert_bytes_mxfp8(H, I) bytes each,
+ * not overlapping; a pure byte permutation, so unpack(pack(b)) == b.  A
+ * device blob with an MXFP8 shared expert is the E packed MXFP4 experts
+ * followed by this expert's packed bytes.
+ */
+int moe_pack_mxfp8(const uint8_t* src_canonical, uint64_t src_bytes, int32_t hidden, int32_t inter,
+                   uint8_t* dst_device_layout, uint64_t dst_bytes);
+int moe_unpack_mxfp8(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t hidden, int32_t inter,
+                     uint8_t* dst_canonical, uint64_t dst_bytes);
 
 /*
  * Routing ("Model techniques map -- DeepSeek-V4-Flash", Checked in its code,

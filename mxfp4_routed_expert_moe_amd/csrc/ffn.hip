@@ -108,7 +108,7 @@ size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8) {
 
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, bool split_fp8, hipStream_t s) {
+                      void* ws, int phase, bool split_fp8, bool shared_w8, hipStream_t s) {
   const int bm = ffn_bm(T, E, k, H, I);
   const int max_items = ffn_max_items(T, E, k, bm);
   const bool dec = use_decode(T, E, k, H, I);
@@ -124,14 +124,15 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
       const uint16_t* act = gateup ? x : w.h;
       const int32_t* rt = gateup ? row_token : nullptr;
       if (dec) {
-        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, s);
+        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, shared_w8, s);
       } else if (split) {
         // phase 1 splits x, then writes h split; phase 2 reads it
         if (gateup) launch_quant_act(x, T, H, w.xq, s);
         launch_ffn_prefill_f8(gateup, gateup ? w.xq : w.hq, rt, w, blob, expert_bytes, H, I, limit, out_rows,
                               max_items, s);
       } else {
-        launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, s);
+        launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, T, E, shared_w8,
+                           s);
       }
     }
   }

@@ -26,6 +26,9 @@ struct FfnWs {
 
 constexpr int kDecodeRows = 16;    // rows per decode item
 constexpr int kPrefillRows = 64;   // rows per prefill item
+// Extra rows of blocks in the prefill grids: their XCD-aware block order
+// reaches every logical block only with at least 8 * ceil(n / 8) blocks.
+constexpr int kGridSlack = 7;
 
 // K sizes with a compiled decode variant (k tiles per wave: K / 512 with
 // four K-splitting waves, one of 1, 2, 4, 8).
@@ -36,10 +39,10 @@ inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K 
 // walks the work list (grid (column blocks, max_items), surplus blocks return).
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
                        int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
-                       float* out_rows, hipStream_t s);
+                       float* out_rows, bool shared_w8, hipStream_t s);
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
-                        hipStream_t s);
+                        int T, int E, bool shared_w8, hipStream_t s);
 void launch_quant_act(const uint16_t* src, int rows, int K, const QAct& dst, hipStream_t s);
 void launch_ffn_prefill_f8(bool gateup, const QAct& aq, const int32_t* row_token, const FfnWs& w,
                            const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows,

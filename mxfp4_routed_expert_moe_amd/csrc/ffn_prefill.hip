@@ -31,7 +31,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
 constexpr int kWavesM = 1, kWavesN = 4;        // 4 waves side by side along the columns
 constexpr int kThreads = 64 * kWavesM * kWavesN;
-constexpr int kNT = 16 / kWavesN;                // weight n-tiles per wave
+constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXFP4)
 constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chunks per lane per tile
 
 // grid (n blocks, max items) of 256 threads = 4 waves side by side, two
@@ -61,33 +61,45 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 // blocks go to the 8 XCDs round robin, and block b takes logical work
 // b % 8 * ceil(total / 8) + b / 8, so consecutive logical blocks (the column
 // blocks of one item, then the next item of the same expert) share an L2.
-template <bool GATEUP>
+// That covers every logical block only if the grid has at least
+// 8 * ceil(total / 8) blocks: launches add kGridSlack rows of blocks.
+//
+// W8: the items of an MXFP8 shared expert (group skip_g of the MXFP4 launch),
+// which are the last n_w8 items of the work list.  Its 2048-byte weight
+// tiles are read as two 1 KiB halves, and a wave takes 2 n-tiles instead of 4
+// so that the register ring keeps its size (a block: 64 rows x 128 columns).
+template <bool GATEUP, bool W8>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
                                                              const int32_t* __restrict__ n_items,
                                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes,
-                                                             int H, int I, float limit, uint16_t* __restrict__ h_out,
+                                                             int H, int I, float limit, int skip_g, int n_w8,
+                                                             uint16_t* __restrict__ h_out,
                                                              float* __restrict__ out_rows) {
+  constexpr int kNT = W8 ? 2 : kNT4;  // weight n-tiles per wave
+  constexpr int NQ = W8 ? 2 : 1;      // 16-byte loads per lane per n-tile per k tile
+  constexpr uint64_t kTileBytes = W8 ? 2048 : 1024;
   __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
   const int nbc = gridDim.x;
-  const int total = *n_items * nbc;
+  const int total = (W8 ? n_w8 : *n_items) * nbc;
   const int b = blockIdx.x + blockIdx.y * nbc;
   const int per = (total + 7) >> 3;
   if ((b >> 3) >= per) return;
   const int lam = (b & 7) * per + (b >> 3);
   if (lam >= total) return;
-  const int4 it = items[lam / nbc];
+  const int4 it = items[(W8 ? *n_items - n_w8 : 0) + lam / nbc];
   const int nb = lam % nbc;
   const int g = it.x, row0 = it.y, nrows = it.z;
+  if (!W8 && g == skip_g) return;  // the MXFP8 shared expert's items run in their own launch
   const int K = GATEUP ? H : I;
   const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const ExpertPlanes pl = expert_planes(H, I);
+  const ExpertPlanes pl = W8 ? expert_planes8(H, I) : expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
-  const uint64_t tstride = static_cast<uint64_t>(KT) * 1024;  // bytes between n-tiles
+  const uint64_t tstride = static_cast<uint64_t>(KT) * kTileBytes;  // bytes between n-tiles
   const uint64_t sstride = static_cast<uint64_t>(KT >> 2) * 256;
 
   const uint8_t* nb0;
@@ -95,13 +107,13 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   const uint8_t* sb0;
   const uint8_t* sb1;
   if (GATEUP) {
-    const int nt0 = nb * 8 + wn * (kNT / 2);  // kNT/2 gate then kNT/2 up n-tiles of the same columns
+    const int nt0 = nb * 2 * kNT + wn * (kNT / 2);  // kNT/2 gate then kNT/2 up n-tiles of the same columns
     nb0 = eb + pl.gate_nib + nt0 * tstride;
     nb1 = eb + pl.up_nib + nt0 * tstride;
     sb0 = eb + pl.gate_sc + nt0 * sstride;
     sb1 = eb + pl.up_sc + nt0 * sstride;
   } else {
-    const int nt0 = nb * 16 + wn * kNT;
+    const int nt0 = nb * 4 * kNT + wn * kNT;
     nb0 = eb + pl.down_nib + nt0 * tstride;
     nb1 = nb0 + (kNT / 2) * tstride;
     sb0 = eb + pl.down_sc + nt0 * sstride;
@@ -124,11 +136,14 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   }
 
   constexpr int kH = kNT / 2;
-  u32x4 bq[kStages][kNT];
+  u32x4 bq[kStages][kNT][NQ];
   uint32_t sw[kNT], swn[kNT];
   auto issue_tile = [&](int stage, int kt) {
 #pragma unroll
-    for (int j = 0; j < kNT; ++j) bq[stage][j] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * 1024);
+    for (int j = 0; j < kNT; ++j)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        bq[stage][j][q] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes + q * 1024);
 #pragma unroll
     for (int q = 0; q < kDmaOps; ++q)
       __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
@@ -185,7 +200,15 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
         for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
-          const bf16x8 bv = dequant8(bq[i][j][s], scf[j]);
+          // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word
+          // s, or 8 E4M3 codes of words 2 (s % 2), +1 of half s / 2
+          bf16x8 bv;
+          if constexpr (W8) {
+            const u32x4& hw = bq[i][j][s >> 1];
+            bv = dequant8_fp8(hw[2 * (s & 1)], hw[2 * (s & 1) + 1], scf[j]);
+          } else {
+            bv = dequant8(bq[i][j][0][s], scf[j]);
+          }
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
         }
@@ -203,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
     if (GATEUP) {
 #pragma unroll
       for (int j = 0; j < kH; ++j) {
-        const int col = nb * 128 + wn * (16 * kH) + j * 16 + (lane & 15);
+        const int col = nb * (64 * kH) + wn * (16 * kH) + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
@@ -217,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
     } else {
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        const int col = nb * 256 + wn * (16 * kNT) + j * 16 + (lane & 15);
+        const int col = nb * (64 * kNT) + wn * (16 * kNT) + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
@@ -232,15 +255,23 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
-                        hipStream_t s) {
+                        int T, int E, bool shared_w8, hipStream_t s) {
+  // the MXFP8 shared expert's items (the last ceil(T / 64) of the work list) in a launch of their own
+  const int skip = shared_w8 ? E : -1;
+  const int nsh = (T + kPrefillRows - 1) / kPrefillRows;
+  const int ny = max_items + kGridSlack, ny8 = nsh + kGridSlack;
   if (gateup) {
-    dim3 g1(I / 128, max_items);
-    ffn_prefill_kernel<true><<<g1, kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob, eb, H, I, limit, w.h,
-                                                nullptr);
+    ffn_prefill_kernel<true, false><<<dim3(I / 128, ny), kThreads, 0, s>>>(
+        act, row_token, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, w.h, nullptr);
+    if (shared_w8)
+      ffn_prefill_kernel<true, true><<<dim3(I / 64, ny8), kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob,
+                                                                           eb, H, I, limit, -1, nsh, w.h, nullptr);
   } else {
-    dim3 g2(H / 256, max_items);
-    ffn_prefill_kernel<false><<<g2, kThreads, 0, s>>>(act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, nullptr,
-                                                 out_rows);
+    ffn_prefill_kernel<false, false><<<dim3(H / 256, ny), kThreads, 0, s>>>(
+        act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, nullptr, out_rows);
+    if (shared_w8)
+      ffn_prefill_kernel<false, true><<<dim3(H / 128, ny8), kThreads, 0, s>>>(
+          act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, -1, nsh, nullptr, out_rows);
   }
 }
 

@@ -119,7 +119,7 @@ __device__ __forceinline__ int a_slot(int r, int c) { return c ^ ((r >> 1) & 7);
 // Per stage the LDS holds the item's hi and lo rows of one 128-k tile
 // (64 x 128 bytes each, chunk c of row r at slot c ^ ((r / 2) mod 8)) and their
 // scales (4 bytes per row); all three arrive by LDS-DMA.  Pipeline, barriers
-// and block order as in the bf16 prefill kernel.
+// and block order (with its grid slack) as in the bf16 prefill kernel.
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_f8_kernel(QAct aq, const int32_t* __restrict__ row_token,
                                                                  const int4* __restrict__ items,
@@ -339,11 +339,11 @@ void launch_ffn_prefill_f8(bool gateup, const QAct& aq, const int32_t* row_token
                            const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows,
                            int max_items, hipStream_t s) {
   if (gateup) {
-    dim3 g1(I / 128, max_items);
+    dim3 g1(I / 128, max_items + kGridSlack);
     ffn_prefill_f8_kernel<true><<<g1, kThreads, 0, s>>>(aq, row_token, w.items, w.n_items, blob, eb, H, I, limit,
                                                         w.hq, nullptr);
   } else {
-    dim3 g2(H / 256, max_items);
+    dim3 g2(H / 256, max_items + kGridSlack);
     ffn_prefill_f8_kernel<false><<<g2, kThreads, 0, s>>>(aq, nullptr, w.items, w.n_items, blob, eb, H, I, limit,
                                                          QAct{nullptr, nullptr, nullptr}, out_rows);
   }

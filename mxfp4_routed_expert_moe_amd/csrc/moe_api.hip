@@ -21,7 +21,8 @@ int check_experts(const moe_experts* d) {
   if (!d || !d->base) return MOE_EINVAL;
   if (d->abi_version != MOE_ABI_VERSION) return MOE_ELAYOUT;
   if (d->layout != MOE_LAYOUT_GFX950_TILED_V1) return MOE_ELAYOUT;
-  if ((d->flags & ~MOE_FFN_SPLIT_FP8) != 0) return MOE_EINVAL;
+  if ((d->flags & ~(MOE_FFN_SPLIT_FP8 | MOE_SHARED_MXFP8)) != 0) return MOE_EINVAL;
+  if ((d->flags & MOE_FFN_SPLIT_FP8) && (d->flags & MOE_SHARED_MXFP8)) return MOE_EINVAL;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_ESHAPE;
   const uint64_t eb = moe_expert_bytes(d->hidden, d->inter);
   if (eb == 0 || d->expert_bytes != eb) return MOE_ESHAPE;
@@ -131,7 +132,7 @@ int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t t
   return hip_status(moe::launch_ffn(x, T, static_cast<const uint8_t*>(experts->base), experts->expert_bytes,
                                     experts->n_experts, experts->hidden, experts->inter, top_k, offsets, row_token,
                                     clamp_limit, out_rows, ws, phase, (experts->flags & MOE_FFN_SPLIT_FP8) != 0,
-                                    as_stream(stream)));
+                                    (experts->flags & MOE_SHARED_MXFP8) != 0, as_stream(stream)));
 }
 
 }  // namespace

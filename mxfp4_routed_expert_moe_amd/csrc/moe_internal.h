@@ -70,6 +70,19 @@ struct ExpertPlanes {
   uint64_t gate_nib, gate_sc, up_nib, up_sc, down_nib, down_sc;
 };
 
+// The planes of an MXFP8 expert: one code byte per weight, same scale planes.
+__host__ __device__ inline ExpertPlanes expert_planes8(int H, int I) {
+  const uint64_t nh = static_cast<uint64_t>(H) * I;
+  ExpertPlanes p;
+  p.gate_nib = 0;
+  p.gate_sc = nh;
+  p.up_nib = nh + nh / 32;
+  p.up_sc = p.up_nib + nh;
+  p.down_nib = 2 * (nh + nh / 32);
+  p.down_sc = p.down_nib + nh;
+  return p;
+}
+
 __host__ __device__ inline ExpertPlanes expert_planes(int H, int I) {
   const uint64_t nh = static_cast<uint64_t>(H) * I;
   ExpertPlanes p;
@@ -80,6 +93,19 @@ __host__ __device__ inline ExpertPlanes expert_planes(int H, int I) {
   p.down_nib = 2 * (nh / 2 + nh / 32);
   p.down_sc = p.down_nib + nh / 2;
   return p;
+}
+
+// Eight E4M3 codes (two 32-bit words, byte order = k order) times one scale
+// -> eight bf16, the B operand of one 16x16x32 bf16 MFMA.  The hardware
+// convert is exact for every code and scale byte < 255 (checked on the
+// device): an E4M3 value times a power of two has four significant bits.
+__device__ __forceinline__ bf16x8 dequant8_fp8(uint32_t lo, uint32_t hi, float scale) {
+  u32x4 w;
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true));
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
@@ -159,11 +185,12 @@ size_t dispatch_ws_bytes(int T, int E, int k);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t s);
 
-// split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8).
+// split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8);
+// shared_w8: the shared expert is MXFP8 (MOE_SHARED_MXFP8).
 size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8);
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, bool split_fp8, hipStream_t s);
+                      void* ws, int phase, bool split_fp8, bool shared_w8, hipStream_t s);
 
 hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s);

@@ -59,6 +59,52 @@ void permute_projection(const uint8_t* src, uint8_t* dst, int N, int K, int dir)
   }
 }
 
+// Offset in the tiled MXFP8 code plane of canonical bytes (n, k .. k+15) of an
+// [N, K] projection (k a multiple of 16): 2048-byte tiles of 16 rows x 128
+// columns; lane 16g + r holds columns 32g .. 32g+15 in the first KiB of the
+// tile and 32g+16 .. 32g+31 in the second.
+inline uint64_t tiled_code8_index(int K, int n, int k) {
+  const int tile = (n / 16) * (K / 128) + k / 128;
+  const int g = (k % 128) / 32, half = (k % 32) / 16;
+  const int lane = 16 * g + n % 16;
+  return static_cast<uint64_t>(tile) * 2048 + half * 1024 + lane * 16;
+}
+
+void permute_projection8(const uint8_t* src, uint8_t* dst, int N, int K, int dir) {
+  for (int n = 0; n < N; ++n) {
+    for (int k = 0; k < K; k += 16) {
+      const uint64_t c = static_cast<uint64_t>(n) * K + k;
+      const uint64_t t = tiled_code8_index(K, n, k);
+      if (dir > 0) memcpy(dst + t, src + c, 16);
+      else memcpy(dst + c, src + t, 16);
+    }
+  }
+  const uint64_t code_bytes = static_cast<uint64_t>(N) * K;
+  const int groups = K / 32;
+  for (int n = 0; n < N; ++n) {
+    for (int gi = 0; gi < groups; ++gi) {
+      const uint64_t c = code_bytes + static_cast<uint64_t>(n) * groups + gi;
+      const uint64_t t = code_bytes + tiled_sc_index(N, K, n, gi);
+      if (dir > 0) dst[t] = src[c];
+      else dst[c] = src[t];
+    }
+  }
+}
+
+int repack8(const uint8_t* src, uint64_t src_bytes, int32_t H, int32_t I, uint8_t* dst, uint64_t dst_bytes, int dir) {
+  if (!src || !dst) return MOE_EINVAL;
+  if (!shape_ok(H, I)) return MOE_ESHAPE;
+  const uint64_t need = moe_expert_bytes_mxfp8(H, I);
+  if (src_bytes < need || dst_bytes < need) return MOE_EINVAL;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + need && b < a + need) return MOE_EINVAL;  // overlapping buffers
+  const uint64_t pg = static_cast<uint64_t>(I) * H + static_cast<uint64_t>(I) * H / 32;
+  permute_projection8(src, dst, I, H, dir);                    // gate [I, H]
+  permute_projection8(src + pg, dst + pg, I, H, dir);          // up   [I, H]
+  permute_projection8(src + 2 * pg, dst + 2 * pg, H, I, dir);  // down [H, I]
+  return MOE_OK;
+}
+
 int repack(const uint8_t* src, uint64_t src_bytes, int32_t n_total, int32_t H, int32_t I, uint8_t* dst,
            uint64_t dst_bytes, int dir) {
   if (!src || !dst) return MOE_EINVAL;
@@ -97,6 +143,21 @@ int moe_pack_mxfp4(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_t
 int moe_unpack_mxfp4(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_total, int32_t hidden,
                      int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes) {
   return repack(src_device_layout, src_bytes, n_total, hidden, inter, dst_canonical, dst_bytes, -1);
+}
+
+uint64_t moe_expert_bytes_mxfp8(int32_t hidden, int32_t inter) {
+  if (!shape_ok(hidden, inter)) return 0;
+  return 3ull * static_cast<uint64_t>(hidden) * static_cast<uint64_t>(inter) * 33ull / 32ull;
+}
+
+int moe_pack_mxfp8(const uint8_t* src_canonical, uint64_t src_bytes, int32_t hidden, int32_t inter,
+                   uint8_t* dst_device_layout, uint64_t dst_bytes) {
+  return repack8(src_canonical, src_bytes, hidden, inter, dst_device_layout, dst_bytes, +1);
+}
+
+int moe_unpack_mxfp8(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t hidden, int32_t inter,
+                     uint8_t* dst_canonical, uint64_t dst_bytes) {
+  return repack8(src_device_layout, src_bytes, hidden, inter, dst_canonical, dst_bytes, -1);
 }
 
 }  // extern "C"

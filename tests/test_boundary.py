@@ -84,6 +84,41 @@ def test_pack_matches_documented_layout_and_round_trips(shape):
                 assert packed[base + _spec_tiled_offset(N * K // 2, N, K, n, k, True)] == blob[c_sc]
 
 
+def _spec_tiled8_offset(N, K, n, k, scale):
+    """Where the device layout puts canonical MXFP8 code (n, k) (or its scale),
+    from the description in include/moe.h, as an offset within the projection."""
+    if scale:
+        return N * K + _spec_tiled_offset(N * K // 2, N, K, n, k, True) - N * K // 2
+    tile = (n // 16) * (K // 128) + k // 128
+    g, half, r = (k % 128) // 32, (k % 32) // 16, n % 16
+    return tile * 2048 + half * 1024 + (16 * g + r) * 16 + k % 16
+
+
+@pytest.mark.parametrize("shape", [(512, 512), (1024, 512), (512, 1536)])
+def test_pack_mxfp8_matches_documented_layout_and_round_trips(shape):
+    H, I = shape
+    blob = WL.make_shared_mxfp8(9, H, I, scale_lo=0, scale_hi=255)
+    assert blob.nbytes == B.lib().moe_expert_bytes_mxfp8(H, I) == 3 * H * I * 33 // 32
+    packed = B.pack_mxfp8(blob, H, I)
+    assert not np.array_equal(packed, blob) and np.array_equal(np.sort(packed), np.sort(blob))
+    assert np.array_equal(B.unpack_mxfp8(packed, H, I), blob)
+    g = np.random.default_rng(1)
+    base = 0
+    for N, K in ((I, H), (I, H), (H, I)):
+        for _ in range(300):
+            n, k = int(g.integers(N)), int(g.integers(K))
+            assert packed[base + _spec_tiled8_offset(N, K, n, k, False)] == blob[base + n * K + k]
+            assert packed[base + _spec_tiled8_offset(N, K, n, k, True)] == blob[base + N * K + n * (K // 32) + k // 32]
+        base += N * K + N * K // 32
+    L = B.lib()
+    n = blob.nbytes
+    out = np.empty_like(blob)
+    assert L.moe_pack_mxfp8(blob.ctypes.data, n - 1, H, I, out.ctypes.data, n) == EINVAL
+    assert L.moe_pack_mxfp8(blob.ctypes.data, n, H, I + 1, out.ctypes.data, n) == ESHAPE
+    assert L.moe_pack_mxfp8(blob.ctypes.data, n, H, I, blob.ctypes.data + 16, n) == EINVAL  # overlap
+    assert L.moe_expert_bytes_mxfp8(4096, 2048) == 25_952_256 and L.moe_expert_bytes_mxfp8(4000, 2048) == 0
+
+
 def test_pack_rejects_bad_arguments():
     L = B.lib()
     a = np.zeros(B.expert_bytes(512, 512) * 2, dtype=np.uint8)
@@ -178,7 +213,9 @@ def test_ffn_checks():
     assert _ffn(d=_desc(expert_bytes=13_369_344 + 32)) == ESHAPE
     assert _ffn(d=_desc(hidden=4000)) == ESHAPE
     assert _ffn(d=_desc(n_experts=0)) == ESHAPE
-    assert _ffn(d=_desc(flags=2)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
+    assert _ffn(d=_desc(flags=4)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
+    assert _ffn(d=_desc(flags=B.MOE_FFN_SPLIT_FP8 | B.MOE_SHARED_MXFP8)) == EINVAL  # not combinable
+    assert _ffn(d=_desc(flags=B.MOE_SHARED_MXFP8), T=0) == OK
     assert _ffn(d=_desc(base=FAKE + 128)) == EALIGN
     assert _ffn(d=_desc(base=None)) == EINVAL
     assert _ffn(k=0) == ESHAPE and _ffn(k=9) == ESHAPE

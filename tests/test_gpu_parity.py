@@ -403,3 +403,78 @@ def test_split_fp8_full_prefill_workloads(index, sample):
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r
     torch.cuda.empty_cache()
+
+
+# The shared expert in MXFP8 (MOE_SHARED_MXFP8).
+def _shared8_inputs(T, H, I, E, seed, routing="learned"):
+    inp = _small_inputs(T, H, I, E, seed, routing)
+    inp.experts = WL.make_experts_shared_mxfp8(seed, E, H, I)
+    return inp
+
+
+@pytest.mark.parametrize("T,H,I,E,routing", [
+    (5, 512, 1024, 16, "learned"),     # decode, one chunk of the shared group
+    (37, 512, 512, 16, "learned"),     # decode, the shared group spans 3 chunks
+    (61, 1024, 512, 64, "hash"),       # decode, hash routing
+    (300, 512, 512, 16, "learned"),    # prefill, ragged 64-row items
+    (200, 1024, 2048, 32, "learned"),  # prefill, K = 1024 and 2048
+])
+def test_shared_mxfp8_small_shapes(T, H, I, E, routing):
+    print(f"[parity] shared mxfp8 T={T} H={H} I={I} E={E} {routing}", flush=True)
+    inp = _shared8_inputs(T, H, I, E, 1000 + T, routing)
+    ex = B.Experts.from_canonical(inp.experts, E, H, I, shared_mxfp8=True)
+    r = LC.full_check(inp, ex, shared_fmt="mxfp8")
+    assert r["ambiguous"] == 0
+    g = r["g"]
+    ref = O.moe_layer(inp.x, inp.experts, n_experts=E, hidden=H, inter=I, top_k=6, route_scale=1.5,
+                      limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table,
+                      shared_fmt="mxfp8")
+    n = int(ref["offsets"][-1])
+    LC.assert_output_close(LC.host(g["out_rows"][:n]), ref["out_rows"], "all rows")
+    LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
+
+
+def _mxfp8_reencode_shared(blob, E, H, I):
+    """The MXFP4 shared expert re-encoded as MXFP8 (same values, same scales)."""
+    eb = WL.expert_bytes(H, I)
+    off = WL.expert_plane_offsets(H, I)
+    e2m1 = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    code8 = e2m1.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    parts = [blob[:E * eb]]
+    for name, n, k in (("gate", I, H), ("up", I, H), ("down", H, I)):
+        nib = blob[E * eb + off[name + "_nib"]: E * eb + off[name + "_nib"] + n * k // 2].reshape(n, k // 2)
+        codes = np.empty((n, k), dtype=np.uint8)
+        codes[:, 0::2] = code8[nib & 0x0F]
+        codes[:, 1::2] = code8[nib >> 4]
+        parts += [codes.ravel(), blob[E * eb + off[name + "_sc"]: E * eb + off[name + "_sc"] + n * k // 32]]
+    return np.concatenate(parts)
+
+
+# decode; prefill; prefill with a shared-expert grid of 4 x 5 blocks (fewer
+# than 8 * ceil(20 / 8): the block order's coverage needs the grid slack)
+@pytest.mark.parametrize("T,H", [(37, 1024), (300, 1024), (300, 512)])
+def test_shared_mxfp8_reencoding_is_bit_identical(T, H):
+    # the same weights as MXFP4 and as MXFP8 decode to the same bf16 values and
+    # are summed in the same order, so the layer must not change by one bit
+    I, E = 512, 16
+    inp = _small_inputs(T, H, I, E, 500 + T)
+    a = LC.run_gpu_layer(inp, _experts(inp))
+    b8 = _mxfp8_reencode_shared(inp.experts, E, H, I)
+    b = LC.run_gpu_layer(inp, B.Experts.from_canonical(b8, E, H, I, shared_mxfp8=True))
+    n = int(a["offsets"][-1])
+    assert torch.equal(a["out_rows"][:n], b["out_rows"][:n]) and np.array_equal(a["y"], b["y"])
+
+
+@pytest.mark.parametrize("index,sample", [(1, 12), (3, 8)])
+def test_shared_mxfp8_full_workloads(index, sample):
+    w = WL.WORKLOADS[index]
+    print(f"[parity] shared mxfp8 full workload {w.name} T={w.T}", flush=True)
+    _EXPERTS_CACHE.clear()
+    canon = WL.make_experts_shared_mxfp8(w.seed, WL.N_EXPERTS)
+    inp = WL.make_layer_inputs(w, experts=canon)
+    ex = B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, shared_mxfp8=True)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, shared_fmt="mxfp8")
+    print(f"[parity] shared mxfp8 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
+    del r, ex
+    torch.cuda.empty_cache()

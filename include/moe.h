@@ -76,6 +76,11 @@ extern "C" {
  */
 #define MOE_SHARED_MXFP8 2
 
+/* Largest token count T any call accepts (MOE_ESHAPE beyond; the workspace
+ * size queries return 0): it keeps every launch's grid within the device's
+ * limits and every row count T * (top_k + 1) in 32 bits. */
+#define MOE_MAX_TOKENS 262144
+
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = 1,      /* NULL pointer, negative size, inconsistent arguments */

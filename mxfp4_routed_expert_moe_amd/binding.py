@@ -22,6 +22,7 @@ MOE_LAYOUT_CANONICAL_MXFP4 = 0x4D584330
 MOE_LAYOUT_GFX950_TILED_V1 = 0x4D584731
 MOE_FFN_SPLIT_FP8 = 1  # moe_experts.flags: prefill expert FFN on the scaled FP4 matrix cores
 MOE_SHARED_MXFP8 = 2   # moe_experts.flags: the shared expert is MXFP8
+MOE_MAX_TOKENS = 262144  # largest T any call accepts
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "MOE_ESHAPE",
           5: "MOE_EWORKSPACE", 6: "MOE_EHIP"}
 

@@ -10,6 +10,7 @@ namespace {
 constexpr int kMaxTopK = 8;
 constexpr int kMaxRouteExperts = 256;
 constexpr int kMaxExperts = 1023;
+constexpr int32_t kMaxTokens = MOE_MAX_TOKENS;  // keeps every grid dimension and 32-bit row count in range
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -65,7 +66,7 @@ int moe_experts_init(moe_experts* d, const void* base, int32_t n_experts, int32_
 }
 
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E) {
-  if (T <= 0 || H <= 0 || H % 512 != 0 || E <= 0) return 0;
+  if (T <= 0 || T > kMaxTokens || H <= 0 || H % 512 != 0 || E <= 0) return 0;
   return static_cast<size_t>(moe::route_hsplit(T, H)) * static_cast<size_t>(T) * static_cast<size_t>(E) * sizeof(double);
 }
 
@@ -73,6 +74,7 @@ int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, co
               const int32_t* token_ids, const int32_t* hash_table, int32_t V, int32_t E, int32_t top_k,
               float route_scale, int32_t* ids, float* weights, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
   if (top_k < 1 || top_k > kMaxTopK || E < top_k || E > kMaxRouteExperts) return MOE_ESHAPE;
   if (!(route_scale == route_scale)) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
@@ -93,13 +95,14 @@ int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, co
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t E, int32_t top_k) {
-  if (T <= 0 || E <= 0 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK) return 0;
+  if (T <= 0 || T > kMaxTokens || E <= 0 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK) return 0;
   return moe::dispatch_ws_bytes(T, E, top_k);
 }
 
 int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_t* offsets, int32_t* row_token,
                  int32_t* slot_row, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
   if (top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxExperts) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!ids || !offsets || !row_token || !slot_row || !ws) return MOE_EINVAL;
@@ -109,7 +112,7 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
 }
 
 size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k) {
-  if (T <= 0 || top_k < 1 || top_k > kMaxTopK || check_experts(experts) != MOE_OK) return 0;
+  if (T <= 0 || T > kMaxTokens || top_k < 1 || top_k > kMaxTopK || check_experts(experts) != MOE_OK) return 0;
   return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k,
                            (experts->flags & MOE_FFN_SPLIT_FP8) != 0);
 }
@@ -120,6 +123,7 @@ int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t t
              const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes, int32_t phase,
              void* stream) {
   if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
   const int st = check_experts(experts);
   if (st != MOE_OK) return st;
   if (top_k < 1 || top_k > kMaxTopK) return MOE_ESHAPE;
@@ -152,6 +156,7 @@ int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* expert
 int moe_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
                 int32_t top_k, uint16_t* y, void* stream) {
   if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
   if (top_k < 1 || top_k > kMaxTopK || H <= 0 || H % 8 != 0) return MOE_ESHAPE;
   if (T == 0) return MOE_OK;
   if (!out_rows || !slot_row || !weights || !y) return MOE_EINVAL;

@@ -168,6 +168,8 @@ def _route(T=4, H=4096, x=FAKE, w=FAKE, bias=None, tok=None, table=None, V=0, E=
 def test_route_checks():
     assert _route(T=0) == OK                      # no-op
     assert _route(T=-1) == EINVAL
+    assert _route(T=B.MOE_MAX_TOKENS + 1) == ESHAPE and B.lib().moe_route_workspace_size(B.MOE_MAX_TOKENS + 1,
+                                                                                        4096, 256) == 0
     assert _route(k=0) == ESHAPE and _route(k=9) == ESHAPE
     assert _route(E=5) == ESHAPE and _route(E=257) == ESHAPE
     assert _route(scale=float("nan")) == EINVAL
@@ -190,6 +192,7 @@ def _dispatch(T=64, E=256, k=6, ids=FAKE, off=FAKE, rt=FAKE, sr=FAKE, ws=FAKE, w
 def test_dispatch_checks():
     assert _dispatch(T=0) == OK
     assert _dispatch(T=-3) == EINVAL
+    assert _dispatch(T=B.MOE_MAX_TOKENS + 1) == ESHAPE
     assert _dispatch(k=0) == ESHAPE and _dispatch(E=0) == ESHAPE and _dispatch(E=1024) == ESHAPE
     for name in ("ids", "off", "rt", "sr", "ws"):
         assert _dispatch(**{name: None}) == EINVAL
@@ -214,6 +217,8 @@ def test_ffn_checks():
     assert _ffn(d=_desc(hidden=4000)) == ESHAPE
     assert _ffn(d=_desc(n_experts=0)) == ESHAPE
     assert _ffn(d=_desc(flags=4)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
+    assert _ffn(T=B.MOE_MAX_TOKENS + 1) == ESHAPE
+    assert B.lib().moe_ffn_workspace_size(B.MOE_MAX_TOKENS + 1, ctypes.byref(_desc()), 6) == 0
     assert _ffn(d=_desc(flags=B.MOE_FFN_SPLIT_FP8 | B.MOE_SHARED_MXFP8)) == EINVAL  # not combinable
     assert _ffn(d=_desc(flags=B.MOE_SHARED_MXFP8), T=0) == OK
     assert _ffn(d=_desc(base=FAKE + 128)) == EALIGN
@@ -244,7 +249,7 @@ def test_combine_checks():
         None if o is None else v(o), None if s is None else v(s), None if w is None else v(w), T, H, k,
         None if y is None else v(y), None)
     assert f(T=0) == OK and f(T=-1) == EINVAL
-    assert f(k=0) == ESHAPE and f(H=4095) == ESHAPE
+    assert f(k=0) == ESHAPE and f(H=4095) == ESHAPE and f(T=B.MOE_MAX_TOKENS + 1) == ESHAPE
     assert f(o=None) == EINVAL and f(s=None) == EINVAL and f(w=None) == EINVAL and f(y=None) == EINVAL
     assert f(o=FAKE_MIS) == EALIGN and f(y=FAKE_MIS) == EALIGN
 

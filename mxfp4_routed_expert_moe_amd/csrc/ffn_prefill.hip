@@ -66,8 +66,9 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 //
 // W8: the items of an MXFP8 shared expert (group skip_g of the MXFP4 launch),
 // which are the last n_w8 items of the work list.  Its 2048-byte weight
-// tiles are read as two 1 KiB halves, and a wave takes 2 n-tiles instead of 4
-// so that the register ring keeps its size (a block: 64 rows x 128 columns).
+// tiles are read as two 1 KiB halves into a two-stage register ring (the
+// same registers as four MXFP4 stages), one tile ahead: each tile drains the
+// wave's loads and passes the barrier, then issues the next tile.
 template <bool GATEUP, bool W8>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
@@ -77,7 +78,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
                                                              int H, int I, float limit, int skip_g, int n_w8,
                                                              uint16_t* __restrict__ h_out,
                                                              float* __restrict__ out_rows) {
-  constexpr int kNT = W8 ? 2 : kNT4;  // weight n-tiles per wave
+  constexpr int kNT = kNT4;           // weight n-tiles per wave
   constexpr int NQ = W8 ? 2 : 1;      // 16-byte loads per lane per n-tile per k tile
   constexpr uint64_t kTileBytes = W8 ? 2048 : 1024;
   __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   }
 
   constexpr int kH = kNT / 2;
-  u32x4 bq[kStages][kNT][NQ];
+  u32x4 bq[W8 ? 2 : kStages][kNT][NQ];  // W8: a two-stage ring (twice the bytes per tile)
   uint32_t sw[kNT], swn[kNT];
   auto issue_tile = [&](int stage, int kt) {
 #pragma unroll
@@ -161,62 +162,88 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_scales(sw, 0);
-  issue_tile(0, 0);
-  issue_tile(1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-
   const int arow = wm * 64 + (lane & 15);
   const int g4 = lane >> 4;
   const int groups = KT >> 2;
-  for (int u = 0; u < groups; ++u) {
-    const bool last = u + 1 == groups;
+  // Tile kt = 4u + i from LDS stage st and register stage sb (scale byte i).
+  auto compute_tile = [&](int i, int st, int sb) {
+    float scf[kNT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kt = 4 * u + i;
-      // Every second tile: tiles kt and kt+1 (issued two tiles ago) are the
-      // last ops issued, so the wave drains its counter; the barrier then
-      // publishes all waves' DMA writes of both and frees the two stages of
-      // tiles kt-2, kt-1 for tiles kt+2, kt+3.
-      if ((i & 1) == 0) {
+    for (int j = 0; j < kNT; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
+    const uint16_t* abuf = As[st];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 a[4];
+      const int slot = ((4 * g4 + s) ^ (lane & 15)) * 8;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word
+        // s, or 8 E4M3 codes of words 2 (s % 2), +1 of half s / 2
+        bf16x8 bv;
+        if constexpr (W8) {
+          const u32x4& hw = bq[sb][j][s >> 1];
+          bv = dequant8_fp8(hw[2 * (s & 1)], hw[2 * (s & 1) + 1], scf[j]);
+        } else {
+          bv = dequant8(bq[sb][j][0][s], scf[j]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
+      }
+    }
+  };
+  if constexpr (W8) {
+    issue_scales(sw, 0);
+    issue_tile(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < groups; ++u) {
+      const bool last = u + 1 == groups;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kt = 4 * u + i;
         wait_vmcnt<0>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if (i == 0 && !last) issue_scales(swn, u + 1);
-        if (kt + 2 < KT) issue_tile((i + 2) % kStages, kt + 2);
-        if (kt + 3 < KT) issue_tile((i + 3) % kStages, kt + 3);
+        if (i == 3 && !last) issue_scales(swn, u + 1);
+        if (kt + 1 < KT) issue_tile((i + 1) & 1, kt + 1);
         __builtin_amdgcn_sched_barrier(0);
+        compute_tile(i, i & 1, i & 1);
       }
-
-      float scf[kNT];
+      if (!last) {
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
-      const uint16_t* abuf = As[i];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 a[4];
-        const int slot = ((4 * g4 + s) ^ (lane & 15)) * 8;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
-#pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word
-          // s, or 8 E4M3 codes of words 2 (s % 2), +1 of half s / 2
-          bf16x8 bv;
-          if constexpr (W8) {
-            const u32x4& hw = bq[i][j][s >> 1];
-            bv = dequant8_fp8(hw[2 * (s & 1)], hw[2 * (s & 1) + 1], scf[j]);
-          } else {
-            bv = dequant8(bq[i][j][0][s], scf[j]);
-          }
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
-        }
+        for (int j = 0; j < kNT; ++j) sw[j] = swn[j];
       }
     }
-    if (!last) {
+  } else {
+    issue_scales(sw, 0);
+    issue_tile(0, 0);
+    issue_tile(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < groups; ++u) {
+      const bool last = u + 1 == groups;
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) sw[j] = swn[j];
+      for (int i = 0; i < 4; ++i) {
+        const int kt = 4 * u + i;
+        // Every second tile: tiles kt and kt+1 (issued two tiles ago) are the
+        // last ops issued, so the wave drains its counter; the barrier then
+        // publishes all waves' DMA writes of both and frees the two stages of
+        // tiles kt-2, kt-1 for tiles kt+2, kt+3.
+        if ((i & 1) == 0) {
+          wait_vmcnt<0>();
+          lds_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          if (i == 0 && !last) issue_scales(swn, u + 1);
+          if (kt + 2 < KT) issue_tile((i + 2) % kStages, kt + 2);
+          if (kt + 3 < KT) issue_tile((i + 3) % kStages, kt + 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        compute_tile(i, i, i);
+      }
+      if (!last) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) sw[j] = swn[j];
+      }
     }
   }
 
@@ -264,13 +291,13 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
     ffn_prefill_kernel<true, false><<<dim3(I / 128, ny), kThreads, 0, s>>>(
         act, row_token, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, w.h, nullptr);
     if (shared_w8)
-      ffn_prefill_kernel<true, true><<<dim3(I / 64, ny8), kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob,
+      ffn_prefill_kernel<true, true><<<dim3(I / 128, ny8), kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob,
                                                                            eb, H, I, limit, -1, nsh, w.h, nullptr);
   } else {
     ffn_prefill_kernel<false, false><<<dim3(H / 256, ny), kThreads, 0, s>>>(
         act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, nullptr, out_rows);
     if (shared_w8)
-      ffn_prefill_kernel<false, true><<<dim3(H / 128, ny8), kThreads, 0, s>>>(
+      ffn_prefill_kernel<false, true><<<dim3(H / 256, ny8), kThreads, 0, s>>>(
           act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, -1, nsh, nullptr, out_rows);
   }
 }

@@ -214,9 +214,12 @@ def route_hash(token_ids, table, top_k: int, route_scale: float):
 
 def boundary_gap(x_bits, w_router, bias, top_k: int) -> np.ndarray:
     """Per token, key[k-th] - key[(k+1)-th] (float64).  A tiny gap means the
-    selection sits on a near tie and either set is a correct answer."""
+    selection sits on a near tie and either set is a correct answer.  With
+    top_k equal to the expert count every expert is chosen: no boundary, gap +inf."""
     s = sqrt_softplus(router_logits(x_bits, w_router))
     key = s if bias is None else s + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    if top_k >= key.shape[1]:
+        return np.full(key.shape[0], np.inf)
     part = -np.sort(-key, axis=1)
     return part[:, top_k - 1] - part[:, top_k]
 

@@ -493,3 +493,15 @@ def test_mxfp8_workload_codes_and_scales():
     assert counts.min() > 0 or set(np.flatnonzero(counts == 0)) == {0x7F, 0xFF}
     sc = b[n: n + n // 32]
     assert sc.min() == 113 and sc.max() == 117
+
+
+def test_top_k_equal_to_expert_count_selects_all():
+    # every expert chosen, in descending key order, weights summing to 1.5; no near-tie boundary
+    T, H, E = 5, 512, 7
+    x = WL.make_x(3, T, H)
+    w = WL.make_router(3, H, E)
+    ids, wt, s = O.route_learned(x, w, None, E, 1.5)
+    assert all(sorted(r) == list(range(E)) for r in ids.tolist())
+    assert np.all(np.diff(np.take_along_axis(s, ids.astype(np.int64), axis=1), axis=1) <= 0)
+    assert np.allclose(wt.sum(axis=1), 1.5, rtol=0, atol=1e-12)
+    assert np.all(np.isinf(O.boundary_gap(x, w, None, E)))

@@ -17,7 +17,7 @@ from tests import layer_check as LC  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-def _cases(n=14, seed=2024):
+def _cases(n=24, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):

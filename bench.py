@@ -104,7 +104,7 @@ def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4"):
 def main():
     args = _parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -30,6 +30,27 @@ constexpr int kPrefillRows = 64;   // rows per prefill item
 // reaches every logical block only with at least 8 * ceil(n / 8) blocks.
 constexpr int kGridSlack = 7;
 
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block barrier for the activation ring.  Unlike __syncthreads() it does not
+// drain the vector-memory counter, so the prefetched tiles stay in flight
+// across it.  No release fence is needed: the only LDS writes are LDS-DMA
+// loads, which each wave has already waited for explicitly (wait_vmcnt), and
+// every LDS read before it has been consumed by an MFMA.  The acquire fence
+// keeps later LDS reads below the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // K sizes with a compiled decode variant (k tiles per wave: K / 512 with
 // four K-splitting waves, one of 1, 2, 4, 8).
 inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }

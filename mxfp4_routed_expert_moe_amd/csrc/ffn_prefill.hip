@@ -7,27 +7,6 @@ namespace moe {
 
 namespace {
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
-// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Block barrier for the activation ring.  Unlike __syncthreads() it does not
-// drain the vector-memory counter, so the prefetched tiles stay in flight
-// across it.  No release fence is needed: the only LDS writes are LDS-DMA
-// loads, which each wave has already waited for explicitly (wait_vmcnt), and
-// every LDS read before it has been consumed by an MFMA.  The acquire fence
-// keeps later LDS reads below the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (register) tiles
 constexpr int kWavesM = 1, kWavesN = 4;        // 4 waves side by side along the columns
 constexpr int kThreads = 64 * kWavesM * kWavesN;

@@ -20,21 +20,6 @@ namespace moe {
 
 namespace {
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Block barrier that does not drain the vector-memory counter (see the bf16
-// prefill kernel); the acquire fence keeps later LDS reads below it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------

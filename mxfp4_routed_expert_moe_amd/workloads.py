@@ -117,6 +117,20 @@ def make_router(seed: int, hidden: int = HIDDEN, n_experts: int = N_EXPERTS) -> 
     return (g.standard_normal((hidden, n_experts), dtype=np.float32) * np.float32(0.125)).astype(np.float32)
 
 
+def make_mxfp4_expert(seed: int, xid: int, hidden: int = HIDDEN, inter: int = INTER,
+                      scale_lo: int = 118, scale_hi: int = 122) -> np.ndarray:
+    """Canonical bytes of MXFP4 expert xid of make_experts(seed, ...), uint8."""
+    off = expert_plane_offsets(hidden, inter)
+    out = np.empty(expert_bytes(hidden, inter), dtype=np.uint8)
+    g = _rng(seed, 3, xid)
+    for name, n, k in (("gate", inter, hidden), ("up", inter, hidden), ("down", hidden, inter)):
+        o = off[name + "_nib"]
+        out[o:o + n * k // 2] = np.frombuffer(g.bytes(n * k // 2), dtype=np.uint8)
+        o = off[name + "_sc"]
+        out[o:o + n * k // 32] = g.integers(scale_lo, scale_hi + 1, size=n * k // 32, dtype=np.uint8)
+    return out
+
+
 def make_experts(seed: int, n_total: int, hidden: int = HIDDEN, inter: int = INTER,
                  scale_lo: int = 118, scale_hi: int = 122) -> np.ndarray:
     """Canonical MXFP4 blob of n_total experts (routed + shared), uint8.
@@ -128,21 +142,66 @@ def make_experts(seed: int, n_total: int, hidden: int = HIDDEN, inter: int = INT
     subset of it one later reads.
     """
     eb = expert_bytes(hidden, inter)
-    off = expert_plane_offsets(hidden, inter)
     out = np.empty(n_total * eb, dtype=np.uint8)
-    nib_g = inter * hidden // 2
-    sc_g = inter * hidden // 32
-    nib_d = hidden * inter // 2
-    sc_d = hidden * inter // 32
     for xid in range(n_total):
-        g = _rng(seed, 3, xid)
-        base = xid * eb
-        for name, nn, ns in (("gate", nib_g, sc_g), ("up", nib_g, sc_g), ("down", nib_d, sc_d)):
-            o = base + off[name + "_nib"]
-            out[o:o + nn] = np.frombuffer(g.bytes(nn), dtype=np.uint8)
-            o = base + off[name + "_sc"]
-            out[o:o + ns] = g.integers(scale_lo, scale_hi + 1, size=ns, dtype=np.uint8)
+        out[xid * eb:(xid + 1) * eb] = make_mxfp4_expert(seed, xid, hidden, inter, scale_lo, scale_hi)
     return out
+
+
+# Group sizes of the 2-bit affine codec (gate, up, down): "OsaurusAI /
+# DeepSeek-V4-Flash-0731-JANG", Dynamic affine recipe.
+AFFINE2_GROUPS = (64, 64, 32)
+
+
+def affine2_projection_bytes(n_out: int, k_in: int, group: int) -> int:
+    """Bytes of one canonical 2-bit affine projection: the code plane (four
+    codes per byte) then the bf16 scale plane and the bf16 bias plane."""
+    return n_out * k_in // 4 + 4 * (n_out * k_in // group)
+
+
+def affine2_expert_bytes(hidden: int, inter: int) -> int:
+    """Bytes of one canonical 2-bit affine expert (gate, up, down)."""
+    gg, gu, gd = AFFINE2_GROUPS
+    return (affine2_projection_bytes(inter, hidden, gg) + affine2_projection_bytes(inter, hidden, gu)
+            + affine2_projection_bytes(hidden, inter, gd))
+
+
+def make_affine2_expert(seed: int, xid: int, hidden: int = HIDDEN, inter: int = INTER) -> np.ndarray:
+    """Canonical bytes of one 2-bit affine routed expert, uint8.
+
+    Per projection [N, K] with group G: the code plane uint8 [N, K/4] (column c
+    in bits 2(c%4)+1 : 2(c%4) of byte c/4; uniform random bytes make every
+    code uniform over 0..3), then scales bf16 [N, K/G], then biases bf16
+    [N, K/G], both little-endian.  Each group draws an exponent u uniform over
+    -8..-4; its scale is 2^u (1 + f/8) with f uniform over 0..7 and its bias
+    -2^u (1 + m/128) with m uniform over 0..127, so the four weight levels of a
+    group straddle zero at about the MXFP4 experts' magnitude.  The bf16 bit
+    patterns are drawn directly (no rounding)."""
+    g = _rng(seed, 5, xid)
+    out = np.empty(affine2_expert_bytes(hidden, inter), dtype=np.uint8)
+    pos = 0
+    for (n, k), gs in zip(((inter, hidden), (inter, hidden), (hidden, inter)), AFFINE2_GROUPS):
+        out[pos:pos + n * k // 4] = np.frombuffer(g.bytes(n * k // 4), dtype=np.uint8)
+        pos += n * k // 4
+        ng = n * k // gs
+        expo = (127 + g.integers(-8, -3, size=ng)).astype(np.uint16)
+        scale = (expo << 7) | (g.integers(0, 8, size=ng).astype(np.uint16) << 4)
+        bias = np.uint16(0x8000) | (expo << 7) | g.integers(0, 128, size=ng).astype(np.uint16)
+        for plane in (scale, bias):
+            out[pos:pos + 2 * ng] = plane.astype("<u2").view(np.uint8)
+            pos += 2 * ng
+    return out
+
+
+def make_experts_affine2(seed: int, n_experts: int, hidden: int = HIDDEN, inter: int = INTER,
+                         shared: str = "mxfp4") -> np.ndarray:
+    """Canonical blob: n_experts 2-bit affine routed experts back to back, then
+    the shared expert (MXFP4 expert n_experts of make_experts(seed, ...), or
+    with shared="mxfp8" the make_shared_mxfp8 expert)."""
+    parts = [make_affine2_expert(seed, xid, hidden, inter) for xid in range(n_experts)]
+    parts.append(make_mxfp4_expert(seed, n_experts, hidden, inter) if shared == "mxfp4"
+                 else make_shared_mxfp8(seed, hidden, inter))
+    return np.concatenate(parts)
 
 
 def mxfp8_expert_bytes(hidden: int, inter: int) -> int:

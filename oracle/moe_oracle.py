@@ -27,6 +27,10 @@ What the layer computes, with the passage each step follows:
   Sizes: E2M1 codes with one E8M0 scale per group of 32 columns).
 * Shared expert and combine (techniques map, row "Shared expert"): the routed
   outputs weighted and summed, plus the shared expert applied to the same input.
+* Optionally the routed experts in the 2-bit affine codec ("OsaurusAI /
+  DeepSeek-V4-Flash-0731-JANG", Dynamic affine recipe): weight = s * q + b
+  with a 2-bit code q and one (s, b) per group of consecutive input columns,
+  64 for gate and up, 32 for down.
 * Optionally the shared expert in MXFP8 ("ElytronAI / DeepSeek-v4-Flash",
   Sizes: the dense weights as E4M3 with one E8M0 scale per 32 columns, the
   mxfp8_lt re-encode), otherwise in MXFP4 like the routed experts.
@@ -37,7 +41,9 @@ column; scale groups run along the input (reduction) axis; ties in the top-6
 go to the lower expert id and the six come out in descending key order;
 softplus is the exact stable form; hash weights are 1.5/6; the shared expert
 has weight 1 and is stored as expert E; h = silu(.)*clamp(.) is rounded to
-bf16 before the down projection; dispatch order is (expert, token, slot).
+bf16 before the down projection; dispatch order is (expert, token, slot);
+affine codes are unsigned, four to a byte with column c in bits 2(c%4)+1:2(c%4)
+of byte c/4, and s, b are bf16 (the codec's scales, biases: MLX affine form).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py
 (closed forms, brute force, invariants).  Full-layer outputs have no worked
@@ -138,6 +144,34 @@ def decode_mxfp8(codes: np.ndarray, scales: np.ndarray, n_out: int, k_in: int) -
     return w.reshape(n_out, k_in)
 
 
+# Group sizes of the 2-bit affine codec, per projection (gate, up, down):
+# "OsaurusAI / DeepSeek-V4-Flash-0731-JANG", Dynamic affine recipe.
+AFFINE2_GROUPS = (64, 64, 32)
+
+
+def decode_affine2(codes: np.ndarray, scales: np.ndarray, biases: np.ndarray, n_out: int, k_in: int,
+                   group: int) -> np.ndarray:
+    """Decode one canonical 2-bit affine projection to float64 [n_out, k_in]:
+    W[r, c] = s[r, c // G] * q[r, c] + b[r, c // G], q the 2-bit code of column c
+    (bits 2(c%4)+1 : 2(c%4) of byte c // 4 of row r), s and b bf16 [n_out, k_in / G].
+    Exact in float64 (q <= 3, s and b have 8 significant bits)."""
+    cb = np.asarray(codes, dtype=np.uint8).reshape(n_out, k_in // 4)
+    q = np.empty((n_out, k_in), dtype=np.float64)
+    for j in range(4):
+        q[:, j::4] = (cb >> (2 * j)) & 3
+    s = bf16_bits_to_f64(np.asarray(scales, dtype=np.uint8).view("<u2").reshape(n_out, k_in // group))
+    b = bf16_bits_to_f64(np.asarray(biases, dtype=np.uint8).view("<u2").reshape(n_out, k_in // group))
+    return (q.reshape(n_out, k_in // group, group) * s[:, :, None] + b[:, :, None]).reshape(n_out, k_in)
+
+
+def canonical_affine2_expert_size(hidden: int, inter: int) -> int:
+    """Bytes of one canonical 2-bit affine expert: per projection its code plane
+    (2 bits per weight) then its bf16 scale plane and bf16 bias plane."""
+    proj = lambda n, k, gs: n * k // 4 + 4 * (n * k // gs)  # noqa: E731
+    gg, gu, gd = AFFINE2_GROUPS
+    return proj(inter, hidden, gg) + proj(inter, hidden, gu) + proj(hidden, inter, gd)
+
+
 def canonical_expert_size(hidden: int, inter: int) -> int:
     """Bytes of one canonical expert (gate, up, down; 4.25 bits per weight)."""
     proj = lambda n, k: n * k // 2 + n * k // 32  # noqa: E731
@@ -150,16 +184,24 @@ def canonical_mxfp8_expert_size(hidden: int, inter: int) -> int:
     return 2 * proj(inter, hidden) + proj(hidden, inter)
 
 
-def decode_expert(blob: np.ndarray, xid: int, hidden: int, inter: int, fmt: str = "mxfp4"):
+def decode_expert(blob: np.ndarray, xid: int, hidden: int, inter: int, fmt: str = "mxfp4",
+                  routed_fmt: str = "mxfp4"):
     """Decode expert xid of a canonical blob -> (gate [I,H], up [I,H], down [H,I]).
 
-    The blob holds MXFP4 experts back to back; fmt = "mxfp8" reads an MXFP8
-    expert starting where MXFP4 expert xid would (the shared expert stored
-    last, after the routed ones)."""
-    eb = canonical_expert_size(hidden, inter)
+    The routed experts sit back to back in routed_fmt ("mxfp4" or "affine2"),
+    so expert xid starts at xid times the size of one routed expert; fmt is the
+    format of expert xid itself ("mxfp8" reads an MXFP8 expert there: the
+    shared expert stored last, after the routed ones)."""
+    eb = canonical_affine2_expert_size(hidden, inter) if routed_fmt == "affine2" else canonical_expert_size(hidden, inter)
     pos = xid * eb
     mats = []
-    for n, k in ((inter, hidden), (inter, hidden), (hidden, inter)):
+    for (n, k), gs in zip(((inter, hidden), (inter, hidden), (hidden, inter)), AFFINE2_GROUPS):
+        if fmt == "affine2":
+            nc, ns = n * k // 4, 2 * (n * k // gs)
+            mats.append(decode_affine2(blob[pos:pos + nc], blob[pos + nc:pos + nc + ns],
+                                       blob[pos + nc + ns:pos + nc + 2 * ns], n, k, gs))
+            pos += nc + 2 * ns
+            continue
         if fmt == "mxfp4":
             nn, ns = n * k // 2, n * k // 32
             mats.append(decode_mxfp4(blob[pos:pos + nn], blob[pos + nn:pos + nn + ns], n, k))
@@ -282,12 +324,13 @@ def expert_forward(xf: np.ndarray, mats, limit: float) -> np.ndarray:
 
 
 def expert_ffn(x_bits, blob, offsets, row_token, limit: float, n_experts: int, hidden: int, inter: int,
-               groups=None, shared_fmt: str = "mxfp4") -> np.ndarray:
+               groups=None, shared_fmt: str = "mxfp4", routed_fmt: str = "mxfp4") -> np.ndarray:
     """Every dispatched row through its expert -> float64 [rows, H].
 
     Expert-major: each group with rows is decoded once, then its rows run.
     `groups` optionally restricts the work to some groups (other rows stay 0);
-    shared_fmt is the weight format of the shared expert (group n_experts).
+    shared_fmt is the weight format of the shared expert (group n_experts),
+    routed_fmt that of the routed ones.
     """
     xf = bf16_bits_to_f64(x_bits)
     offsets = np.asarray(offsets, dtype=np.int64)
@@ -297,7 +340,7 @@ def expert_ffn(x_bits, blob, offsets, row_token, limit: float, n_experts: int, h
         r0, r1 = int(offsets[g]), int(offsets[g + 1])
         if r1 == r0:
             continue
-        mats = decode_expert(blob, g, hidden, inter, shared_fmt if g == n_experts else "mxfp4")
+        mats = decode_expert(blob, g, hidden, inter, shared_fmt if g == n_experts else routed_fmt, routed_fmt)
         out[r0:r1] = expert_forward(xf[row_token[r0:r1]], mats, limit)
     return out
 
@@ -321,7 +364,7 @@ def combine(out_rows: np.ndarray, slot_row: np.ndarray, weights: np.ndarray) -> 
 
 def moe_layer(x_bits, blob, *, n_experts: int, hidden: int, inter: int, top_k: int,
               route_scale: float, limit: float, w_router=None, bias=None, token_ids=None, table=None,
-              shared_fmt: str = "mxfp4"):
+              shared_fmt: str = "mxfp4", routed_fmt: str = "mxfp4"):
     """The whole layer: route -> dispatch -> expert FFN -> combine.  Returns a dict
     with ids, weights, offsets, row_token, slot_row, out_rows and y (float64)."""
     if table is not None:
@@ -329,14 +372,15 @@ def moe_layer(x_bits, blob, *, n_experts: int, hidden: int, inter: int, top_k: i
     else:
         ids, w, _ = route_learned(x_bits, w_router, bias, top_k, route_scale)
     offsets, row_token, slot_row = dispatch(ids, n_experts)
-    out = expert_ffn(x_bits, blob, offsets, row_token, limit, n_experts, hidden, inter, shared_fmt=shared_fmt)
+    out = expert_ffn(x_bits, blob, offsets, row_token, limit, n_experts, hidden, inter, shared_fmt=shared_fmt,
+                     routed_fmt=routed_fmt)
     y = combine(out, slot_row, w)
     return dict(ids=ids, weights=w, offsets=offsets, row_token=row_token, slot_row=slot_row,
                 out_rows=out, y=y)
 
 
 def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, inter: int, limit: float,
-                    shared_fmt: str = "mxfp4"):
+                    shared_fmt: str = "mxfp4", routed_fmt: str = "mxfp4"):
     """Brute force without dispatch: every token through ALL experts, masked by a
     0/1 selection mask and weighted, plus the shared expert.  Tiny inputs only."""
     xf = bf16_bits_to_f64(x_bits)
@@ -347,7 +391,7 @@ def dense_moe_layer(x_bits, blob, ids, weights, *, n_experts: int, hidden: int, 
         mask = (ids == e)                               # [T, k]
         we = (np.asarray(weights, dtype=np.float64) * mask).sum(axis=1)  # 0 where not chosen
         sel = mask.any(axis=1).astype(np.float64)
-        ye = expert_forward(xf, decode_expert(blob, e, hidden, inter), limit)
+        ye = expert_forward(xf, decode_expert(blob, e, hidden, inter, routed_fmt, routed_fmt), limit)
         y += (sel * we)[:, None] * ye
-    y += expert_forward(xf, decode_expert(blob, n_experts, hidden, inter, shared_fmt), limit)
+    y += expert_forward(xf, decode_expert(blob, n_experts, hidden, inter, shared_fmt, routed_fmt), limit)
     return y

@@ -505,3 +505,121 @@ def test_top_k_equal_to_expert_count_selects_all():
     assert np.all(np.diff(np.take_along_axis(s, ids.astype(np.int64), axis=1), axis=1) <= 0)
     assert np.allclose(wt.sum(axis=1), 1.5, rtol=0, atol=1e-12)
     assert np.all(np.isinf(O.boundary_gap(x, w, None, E)))
+
+
+# ---------------------------------------------------------------- 2-bit affine routed experts
+def _bf16_bytes(values):
+    """bf16 bytes (little-endian) of values exactly representable in bf16, via torch."""
+    t = torch.tensor(values, dtype=torch.float64).to(torch.bfloat16)
+    assert torch.equal(t.double(), torch.tensor(values, dtype=torch.float64))
+    return t.view(torch.int16).numpy().astype("<i2").view(np.uint8)
+
+
+@pytest.mark.parametrize("group", [64, 32])
+def test_decode_affine2_bit_fields_and_group_axis(group):
+    # codes written bit by bit in plain Python; s, b per (row, group) chosen so
+    # every weight is a distinct small dyadic number, computed here in Python floats
+    n, k = 3, 128
+    q = [[(7 * r + c * c + c // 5) % 4 for c in range(k)] for r in range(n)]
+    codes = bytearray()
+    for r in range(n):
+        for c0 in range(0, k, 4):
+            byte = 0
+            for j in range(4):
+                byte |= q[r][c0 + j] << (2 * j)          # column c0+j in bits 2j+1:2j
+            codes.append(byte)
+    ng = k // group
+    s = [[2.0 ** (r - gi) * (1 + gi / 8) for gi in range(ng)] for r in range(n)]
+    b = [[-(gi + 1) * 0.25 - r for gi in range(ng)] for r in range(n)]
+    w = O.decode_affine2(np.frombuffer(bytes(codes), dtype=np.uint8), _bf16_bytes(sum(s, [])),
+                         _bf16_bytes(sum(b, [])), n, k, group)
+    want = np.array([[s[r][c // group] * q[r][c] + b[r][c // group] for c in range(k)] for r in range(n)])
+    assert np.array_equal(w, want)
+    # reading the same planes with the other group size must differ (group axis pinned)
+    other = 32 if group == 64 else 64
+    ns = n * k // other
+    alt = O.decode_affine2(np.frombuffer(bytes(codes), dtype=np.uint8), _bf16_bytes([1.0] * ns), _bf16_bytes([0.0] * ns),
+                           n, k, other)
+    assert np.array_equal(alt, np.array(q, dtype=np.float64))     # s = 1, b = 0 gives the codes back
+
+
+def test_affine2_sizes_closed_form():
+    # 2 bits per weight plus a bf16 (scale, bias) per 64 (gate, up) or 32 (down)
+    # weights: (2 + 0.5) + (2 + 0.5) + (2 + 1) bits over three H*I projections = 8 bits per H*I
+    for h, i in ((4096, 2048), (512, 512), (1024, 512)):
+        assert O.canonical_affine2_expert_size(h, i) == h * i == WL.affine2_expert_bytes(h, i)
+    assert O.AFFINE2_GROUPS == WL.AFFINE2_GROUPS == (64, 64, 32)
+
+
+def _affine2_twin(E, hidden, inter, seed):
+    """An affine blob and an MXFP4 blob that hold the same weights: in each
+    affine group s = 2^e, b = -c 2^e (c in 0..3), so w = 2^e (q - c) is an
+    integer in -3..3 times 2^e, which E2M1 codes hold exactly under the MX
+    scale byte e + 127 of both 32-column halves of the group."""
+    rng = np.random.default_rng(seed)
+    e2m1_of_int = {0: 0x0, 1: 0x2, 2: 0x4, 3: 0x5}                  # E2M1 1.0, 2.0, 3.0
+    aff, mx = [], []
+    for xid in range(E):
+        ab, mb = [], []
+        for (n, k), gs in zip(((inter, hidden), (inter, hidden), (hidden, inter)), O.AFFINE2_GROUPS):
+            q = rng.integers(0, 4, size=(n, k))
+            ee = rng.integers(-8, -3, size=(n, k // gs))
+            c = rng.integers(0, 4, size=(n, k // gs))
+            v = q - np.repeat(c, gs, axis=1)                                 # integers -3..3
+            codes = np.zeros((n, k // 4), dtype=np.uint8)
+            for j in range(4):
+                codes |= (q[:, j::4] << (2 * j)).astype(np.uint8)
+            ab += [codes.ravel(), _bf16_bytes((2.0 ** ee).ravel().tolist()),
+                   _bf16_bytes((-c * 2.0 ** ee).ravel().tolist())]
+            nib = np.vectorize(lambda t: e2m1_of_int[abs(t)] | (0x8 if t < 0 else 0))(v).astype(np.uint8)
+            mb += [(nib[:, 0::2] | (nib[:, 1::2] << 4)).ravel(),
+                   (np.repeat(ee, gs // 32, axis=1) + 127).astype(np.uint8).ravel()]
+        aff.append(np.concatenate(ab))
+        mx.append(np.concatenate(mb))
+    shared = WL.make_mxfp4_expert(seed, E, hidden, inter)
+    return np.concatenate(aff + [shared]), np.concatenate(mx + [shared])
+
+
+@pytest.mark.parametrize("routing", ["learned", "hash"])
+def test_affine2_layer_equals_its_mxfp4_twin(routing):
+    # the affine reader (its own layout, groups and bf16 planes) must give the
+    # layer exactly what the pinned MXFP4 reader gives for the same weights
+    T, hidden, inter, E = 9, 128, 64, 16
+    x, _, kw, rk = _tiny_layer(T, hidden, inter, E, 43, routing)
+    ba, bm = _affine2_twin(E, hidden, inter, 43)
+    assert len(ba) == E * O.canonical_affine2_expert_size(hidden, inter) + O.canonical_expert_size(hidden, inter)
+    ra = O.moe_layer(x, ba, **kw, **rk, routed_fmt="affine2")
+    rm = O.moe_layer(x, bm, **kw, **rk)
+    assert np.array_equal(ra["out_rows"], rm["out_rows"]) and np.array_equal(ra["y"], rm["y"])
+
+
+@pytest.mark.parametrize("shared", ["mxfp4", "mxfp8"])
+def test_dense_brute_force_equals_sparse_affine2(shared):
+    T, hidden, inter, E = 8, 128, 64, 16
+    x, _, kw, rk = _tiny_layer(T, hidden, inter, E, 29)
+    blob = WL.make_experts_affine2(29, E, hidden, inter, shared)
+    r = O.moe_layer(x, blob, **kw, **rk, routed_fmt="affine2", shared_fmt=shared)
+    yd = O.dense_moe_layer(x, blob, r["ids"], r["weights"], n_experts=E, hidden=hidden, inter=inter, limit=10.0,
+                           shared_fmt=shared, routed_fmt="affine2")
+    assert np.max(np.abs(yd - r["y"])) <= 1e-12 * np.max(np.abs(yd))
+    # the format matters: the same bytes read as MXFP4 experts give another y
+    assert np.all(np.isfinite(r["y"]))
+    assert not np.allclose(O.expert_forward(O.bf16_bits_to_f64(x), O.decode_expert(blob, 0, hidden, inter, "affine2",
+                                                                                    "affine2"), 10.0),
+                           O.expert_forward(O.bf16_bits_to_f64(x), O.decode_expert(blob, 0, hidden, inter), 10.0))
+
+
+def test_affine2_workload_fields():
+    hidden, inter = 512, 512
+    b = WL.make_affine2_expert(3, 0, hidden, inter)
+    n = inter * hidden
+    codes = b[:n // 4]
+    q = np.stack([(codes >> (2 * j)) & 3 for j in range(4)]).ravel()
+    counts = np.bincount(q, minlength=4)
+    assert counts.min() > 0.24 * q.size                              # uniform over 0..3
+    sc = b[n // 4: n // 4 + 2 * (n // 64)].view("<u2")
+    bi = b[n // 4 + 2 * (n // 64): n // 4 + 4 * (n // 64)].view("<u2")
+    assert np.all(sc >> 15 == 0) and np.all(bi >> 15 == 1)          # scales positive, biases negative
+    assert np.array_equal((sc >> 7) & 0xFF, (bi >> 7) & 0xFF)       # same exponent per group
+    assert set(np.unique((sc >> 7) & 0xFF)) == set(range(119, 124))  # 2^-8 .. 2^-4
+    assert np.all(sc & 0xF == 0)                                     # scale mantissa 1 + f/8

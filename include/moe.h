@@ -76,6 +76,22 @@ extern "C" {
  */
 #define MOE_SHARED_MXFP8 2
 
+/*
+ * moe_experts.flags.  MOE_ROUTED_AFFINE2: the n_experts routed experts are in
+ * the 2-bit affine codec of "OsaurusAI / DeepSeek-V4-Flash-0731-JANG", Dynamic
+ * affine recipe: weight = s * q + b with q an unsigned 2-bit code and one bf16
+ * scale s and one bf16 bias b per group of 64 consecutive input columns (gate,
+ * up) or 32 (down).  expert_bytes must equal moe_expert_bytes_affine2(H, I)
+ * (= H * I: 2.5, 2.5 and 3 bits per weight).  The shared expert, slot
+ * n_experts at base + n_experts * expert_bytes, keeps an MX layout: MXFP4
+ * (moe_expert_bytes(H, I) bytes) or, with MOE_SHARED_MXFP8, MXFP8 -- the
+ * recipe's shared expert is 8-bit.  The FFN runs its decode kernel family at
+ * every token count, so H and I must each be 512, 1024, 2048 or 4096
+ * (MOE_ESHAPE otherwise).  Not combinable with MOE_FFN_SPLIT_FP8 (MOE_EINVAL).
+ * The 3-bit gate of six listed layers in the same recipe is not supported.
+ */
+#define MOE_ROUTED_AFFINE2 4
+
 /* Largest token count T any call accepts (MOE_ESHAPE beyond; the workspace
  * size queries return 0): it keeps every launch's grid within the device's
  * limits and every row count T * (top_k + 1) in 32 bits. */
@@ -132,14 +148,33 @@ uint32_t moe_abi_version(void);
  * 32*g .. +15 of row 16*(n/16) + r) and bytes [1024 + 16l, 1024 + 16l + 16)
  * (columns +16 .. +31); the scale plane is tiled exactly as above.
  */
+/*
+ * A 2-bit affine expert (MOE_ROUTED_AFFINE2) has the three projections gate
+ * [I, H] (group G = 64), up [I, H] (G = 64), down [H, I] (G = 32), each
+ * canonically its code plane uint8 [N][K/4] (byte b of a row: column 4b + j
+ * in bits 2j+1:2j) followed by its scale plane bf16 [N][K/G] and its bias
+ * plane bf16 [N][K/G] (little-endian).  Device layout, per projection at the
+ * same offsets:
+ *   code plane: 512-byte tiles t = (n/16) * (K/128) + (k/128); inside a tile,
+ *     lane l = 16*g + r owns bytes [8l, 8l+8) as two little-endian words; word
+ *     u holds the 16 codes of row 16*(n/16) + r at columns 128*(k/128) +
+ *     32*s + 8*g + i for s in {2u, 2u+1}, i < 8, code (s, i) in bits
+ *     16*(i%2) + 2*(4*(s%2) + i/2) +1 : +0.
+ *   scale and bias planes, together: blocks of 16 * (128/G) * 4 bytes, block
+ *     (n/16) * (K/128) + (k/128); entry (n%16) * (128/G) + (k%128)/G of a
+ *     block is 4 bytes: the bf16 scale, then the bf16 bias, of row n's group
+ *     at column k.
+ * So one 8-byte load per lane gives a wave the codes of a 16-column x 128-k
+ * tile, each group of 8 codes feeding one 16x16x32 MFMA over a single group.
+ */
 typedef struct moe_experts {
   uint32_t abi_version;   /* MOE_ABI_VERSION */
   uint32_t layout;        /* MOE_LAYOUT_GFX950_TILED_V1 for the compute calls */
   int32_t n_experts;      /* routed experts E (blob holds E + 1 experts) */
   int32_t hidden;         /* H */
   int32_t inter;          /* I */
-  int32_t flags;          /* 0, MOE_FFN_SPLIT_FP8 or MOE_SHARED_MXFP8 */
-  uint64_t expert_bytes;  /* must equal moe_expert_bytes(H, I) */
+  int32_t flags;          /* 0 or MOE_FFN_SPLIT_FP8, MOE_SHARED_MXFP8, MOE_ROUTED_AFFINE2 (see each) */
+  uint64_t expert_bytes;  /* moe_expert_bytes(H, I), or moe_expert_bytes_affine2(H, I) */
   const void* base;       /* device pointer, 256-byte aligned */
 } moe_experts;
 
@@ -179,6 +214,23 @@ int moe_pack_mxfp8(const uint8_t* src_canonical, uint64_t src_bytes, int32_t hid
                    uint8_t* dst_device_layout, uint64_t dst_bytes);
 int moe_unpack_mxfp8(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t hidden, int32_t inter,
                      uint8_t* dst_canonical, uint64_t dst_bytes);
+
+/* Bytes of one 2-bit affine expert of shape (H, I): H * I; 0 for unsupported shapes. */
+uint64_t moe_expert_bytes_affine2(int32_t hidden, int32_t inter);
+
+/*
+ * Repack of n_experts 2-bit affine routed experts, canonical <-> device
+ * layout: src and dst are HOST pointers to n_experts *
+ * moe_expert_bytes_affine2(H, I) bytes each, not overlapping.  A permutation
+ * of the 2-bit codes and of the (scale, bias) pairs, so unpack(pack(b)) == b.
+ * A device blob with affine routed experts is their packed bytes followed by
+ * the packed MX shared expert (moe_pack_mxfp4 with n_total = 1, or
+ * moe_pack_mxfp8).  Synchronous; touches no GPU.
+ */
+int moe_pack_affine2(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_experts, int32_t hidden,
+                     int32_t inter, uint8_t* dst_device_layout, uint64_t dst_bytes);
+int moe_unpack_affine2(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_experts, int32_t hidden,
+                       int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes);
 
 /*
  * Routing ("Model techniques map -- DeepSeek-V4-Flash", Checked in its code,
@@ -239,7 +291,9 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
  * for each row p of group e, x = x[row_token[p]].  The MXFP4 weights are
  * decoded to bf16 on the fly and fed to bf16 MFMA (or, with MOE_FFN_SPLIT_FP8
  * in experts->flags and a prefill-sized T, fed as stored to the scaled FP4
- * matrix cores); only the experts that own rows are read.
+ * matrix cores); only the experts that own rows are read.  With
+ * MOE_ROUTED_AFFINE2 each routed projection is computed per group as
+ * s * (x . q) + b * sum(x) (the same sum, regrouped), x . q on bf16 MFMA.
  *
  * x         bf16 [T, H]; experts: descriptor (host pointer) of the device blob
  * offsets, row_token: as written by moe_dispatch for the same T, E, top_k

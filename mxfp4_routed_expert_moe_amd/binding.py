@@ -22,12 +22,15 @@ MOE_LAYOUT_CANONICAL_MXFP4 = 0x4D584330
 MOE_LAYOUT_GFX950_TILED_V1 = 0x4D584731
 MOE_FFN_SPLIT_FP8 = 1  # moe_experts.flags: prefill expert FFN on the scaled FP4 matrix cores
 MOE_SHARED_MXFP8 = 2   # moe_experts.flags: the shared expert is MXFP8
+MOE_ROUTED_AFFINE2 = 4  # moe_experts.flags: the routed experts are 2-bit affine (JANG recipe)
 MOE_MAX_TOKENS = 262144  # largest T any call accepts
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "MOE_ESHAPE",
           5: "MOE_EWORKSPACE", 6: "MOE_EHIP"}
 
 EXPORTED = ("moe_status_str", "moe_abi_version", "moe_expert_bytes", "moe_experts_init", "moe_pack_mxfp4",
-            "moe_unpack_mxfp4", "moe_expert_bytes_mxfp8", "moe_pack_mxfp8", "moe_unpack_mxfp8", "moe_route_workspace_size", "moe_route", "moe_dispatch_workspace_size",
+            "moe_unpack_mxfp4", "moe_expert_bytes_mxfp8", "moe_pack_mxfp8", "moe_unpack_mxfp8",
+            "moe_expert_bytes_affine2", "moe_pack_affine2", "moe_unpack_affine2", "moe_route_workspace_size", "moe_route",
+            "moe_dispatch_workspace_size",
             "moe_dispatch", "moe_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_phase", "moe_combine")
 
 
@@ -65,6 +68,9 @@ def lib() -> ctypes.CDLL:
         "moe_expert_bytes_mxfp8": (c_u64, [c_i32, c_i32]),
         "moe_pack_mxfp8": (ctypes.c_int, [vp, c_u64, c_i32, c_i32, vp, c_u64]),
         "moe_unpack_mxfp8": (ctypes.c_int, [vp, c_u64, c_i32, c_i32, vp, c_u64]),
+        "moe_expert_bytes_affine2": (c_u64, [c_i32, c_i32]),
+        "moe_pack_affine2": (ctypes.c_int, [vp, c_u64, c_i32, c_i32, c_i32, vp, c_u64]),
+        "moe_unpack_affine2": (ctypes.c_int, [vp, c_u64, c_i32, c_i32, c_i32, vp, c_u64]),
         "moe_route_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
         "moe_route": (ctypes.c_int, [vp, c_i32, c_i32, vp, vp, vp, vp, c_i32, c_i32, c_i32, ctypes.c_float,
                                      vp, vp, vp, c_sz, vp]),
@@ -129,6 +135,23 @@ def unpack_mxfp8(device_layout: np.ndarray, hidden: int, inter: int) -> np.ndarr
     return dst
 
 
+def pack_affine2(canonical: np.ndarray, n_experts: int, hidden: int, inter: int) -> np.ndarray:
+    """Canonical 2-bit affine routed experts (uint8, host) -> device layout (uint8, host)."""
+    src = np.ascontiguousarray(canonical, dtype=np.uint8)
+    dst = np.empty_like(src)
+    _check("moe_pack_affine2", lib().moe_pack_affine2(src.ctypes.data, src.nbytes, n_experts, hidden, inter,
+                                                      dst.ctypes.data, dst.nbytes))
+    return dst
+
+
+def unpack_affine2(device_layout: np.ndarray, n_experts: int, hidden: int, inter: int) -> np.ndarray:
+    src = np.ascontiguousarray(device_layout, dtype=np.uint8)
+    dst = np.empty_like(src)
+    _check("moe_unpack_affine2", lib().moe_unpack_affine2(src.ctypes.data, src.nbytes, n_experts, hidden, inter,
+                                                          dst.ctypes.data, dst.nbytes))
+    return dst
+
+
 # ---------------------------------------------------------------- device calls
 def _torch():
     import torch
@@ -161,7 +184,7 @@ class Experts:
     """A device-layout expert blob on the GPU and its C descriptor."""
 
     def __init__(self, blob_device, n_experts: int, hidden: int, inter: int, split_fp8: bool = False,
-                 shared_mxfp8: bool = False):
+                 shared_mxfp8: bool = False, routed_affine2: bool = False):
         torch = _torch()
         _dev(blob_device, torch.uint8, "blob")
         self.blob = blob_device
@@ -169,21 +192,29 @@ class Experts:
         self.desc = moe_experts()
         _check("moe_experts_init", lib().moe_experts_init(ctypes.byref(self.desc), _ptr(blob_device), n_experts,
                                                           hidden, inter))
-        self.desc.flags = (MOE_FFN_SPLIT_FP8 if split_fp8 else 0) | (MOE_SHARED_MXFP8 if shared_mxfp8 else 0)
+        self.desc.flags = ((MOE_FFN_SPLIT_FP8 if split_fp8 else 0) | (MOE_SHARED_MXFP8 if shared_mxfp8 else 0)
+                           | (MOE_ROUTED_AFFINE2 if routed_affine2 else 0))
+        if routed_affine2:
+            self.desc.expert_bytes = int(lib().moe_expert_bytes_affine2(hidden, inter))
 
     @classmethod
     def from_canonical(cls, canonical: np.ndarray, n_experts: int, hidden: int, inter: int, device="cuda",
-                       split_fp8: bool = False, shared_mxfp8: bool = False):
-        """canonical: n_experts + 1 MXFP4 experts, or (shared_mxfp8) n_experts
-        MXFP4 experts followed by one MXFP8 expert."""
+                       split_fp8: bool = False, shared_mxfp8: bool = False, routed_affine2: bool = False):
+        """canonical: n_experts routed experts (MXFP4, or 2-bit affine with
+        routed_affine2) followed by the shared expert (MXFP4, or MXFP8 with
+        shared_mxfp8)."""
         torch = _torch()
-        if shared_mxfp8:
-            nb = n_experts * int(lib().moe_expert_bytes(hidden, inter))
-            packed = np.concatenate([pack_mxfp4(canonical[:nb], n_experts, hidden, inter),
-                                     pack_mxfp8(canonical[nb:], hidden, inter)])
+        if routed_affine2:
+            nb = n_experts * int(lib().moe_expert_bytes_affine2(hidden, inter))
+            routed = pack_affine2(canonical[:nb], n_experts, hidden, inter)
         else:
-            packed = pack_mxfp4(canonical, n_experts + 1, hidden, inter)
-        return cls(torch.from_numpy(packed).to(device), n_experts, hidden, inter, split_fp8, shared_mxfp8)
+            nb = n_experts * int(lib().moe_expert_bytes(hidden, inter))
+            routed = pack_mxfp4(canonical[:nb], n_experts, hidden, inter)
+        shared = pack_mxfp8(canonical[nb:], hidden, inter) if shared_mxfp8 else pack_mxfp4(canonical[nb:], 1, hidden,
+                                                                                           inter)
+        packed = np.concatenate([routed, shared])
+        return cls(torch.from_numpy(packed).to(device), n_experts, hidden, inter, split_fp8, shared_mxfp8,
+                   routed_affine2)
 
 
 def route(x, T: int, E: int, top_k: int, route_scale: float, w_router=None, sel_bias=None, token_ids=None,

@@ -90,28 +90,33 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
 }
 
 // Decode kernels while the average group holds at most ~16 rows (and both K
-// sizes have a compiled decode variant); prefill kernels otherwise.
-inline bool use_decode(int T, int E, int k, int H, int I) {
-  return static_cast<long>(T) * (k + 1) <= 16L * (E + 1) && decode_k_ok(H) && decode_k_ok(I);
+// sizes have a compiled decode variant), and for 2-bit affine routed experts
+// at every T (the validation has checked both K sizes); prefill kernels
+// otherwise.
+inline bool use_decode(int T, int E, int k, int H, int I, bool routed_a2) {
+  return routed_a2 || (static_cast<long>(T) * (k + 1) <= 16L * (E + 1) && decode_k_ok(H) && decode_k_ok(I));
 }
 
-inline int ffn_bm(int T, int E, int k, int H, int I) { return use_decode(T, E, k, H, I) ? kDecodeRows : kPrefillRows; }
+inline int ffn_bm(int T, int E, int k, int H, int I, bool routed_a2) {
+  return use_decode(T, E, k, H, I, routed_a2) ? kDecodeRows : kPrefillRows;
+}
 
 }  // namespace
 
-size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8) {
-  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I));
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool routed_a2) {
+  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I, routed_a2));
   const size_t n = 256 + align256(sizeof(int4) * static_cast<size_t>(mi));
-  if (split_fp8 && !use_decode(T, E, k, H, I)) return n + qact_bytes(T, H) + qact_bytes(static_cast<long>(T) * (k + 1), I);
+  if (split_fp8 && !use_decode(T, E, k, H, I, routed_a2))
+    return n + qact_bytes(T, H) + qact_bytes(static_cast<long>(T) * (k + 1), I);
   return n + align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
 }
 
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, bool split_fp8, bool shared_w8, hipStream_t s) {
-  const int bm = ffn_bm(T, E, k, H, I);
+                      void* ws, int phase, bool split_fp8, bool shared_w8, bool routed_a2, hipStream_t s) {
+  const int bm = ffn_bm(T, E, k, H, I, routed_a2);
   const int max_items = ffn_max_items(T, E, k, bm);
-  const bool dec = use_decode(T, E, k, H, I);
+  const bool dec = use_decode(T, E, k, H, I, routed_a2);
   const bool split = split_fp8 && !dec;
   FfnWs w = ffn_carve(ws, max_items, T, k, H, I, split);
   for (int ph = 0; ph < 3; ++ph) {
@@ -124,7 +129,8 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
       const uint16_t* act = gateup ? x : w.h;
       const int32_t* rt = gateup ? row_token : nullptr;
       if (dec) {
-        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, shared_w8, s);
+        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, shared_w8,
+                          routed_a2, s);
       } else if (split) {
         // phase 1 splits x, then writes h split; phase 2 reads it
         if (gateup) launch_quant_act(x, T, H, w.xq, s);

@@ -172,44 +172,234 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
   }
 }
 
-// grid (n blocks, E + ceil(T / 16)), 64 * kWaves threads: block row y < E takes the
-// rows of routed expert y (16 at a time; an expert with no rows returns at
-// once), the rest take 16-row chunks of the shared group, so the decode path
-// needs no work list.  W8 (MXFP8 shared expert): grid (n blocks, ceil(T / 16))
-// over the shared group only, while the MXFP4 launch then has E block rows.
-// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles; W8: 32, 2 + 2),
+// 2-bit affine codes -> MFMA B operand.  Word w of a tile lane holds the
+// codes of two MFMAs (half = s % 2); pair p of MFMA s sits at bits 2*sigma
+// (even k) and 16 + 2*sigma (odd k), sigma = 4 * half + p.  Shifted to bits
+// 5..6 of each 16-bit half under the bf16 pattern 0x4080 (4.0), a code q
+// becomes the bf16 value 4 + q exactly: eight values 4 + q in k order.
+template <int HALF>
+__device__ __forceinline__ bf16x8 affine2_operand(uint32_t w) {
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    constexpr int kBase = 2 * 4 * HALF - 5;
+    const int sh = kBase + 2 * p;
+    const uint32_t t = sh >= 0 ? (w >> sh) : (w << -sh);
+    o[p] = (t & 0x00600060u) | 0x40804080u;
+  }
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// One chunk of at most 16 rows of 2-bit affine routed expert g.  Per group of
+// G input columns (64 for gate and up, 32 for down), with q the codes and s, b
+// the group's bf16 scale and bias,
+//   sum_k x_k (s q_k + b) = s * (sum_k x_k (4 + q_k)) + (b - 4 s) * sum_k x_k,
+// so the MFMAs run x against the exact bf16 values 4 + q (P) and against ones
+// (S, the row sums of x over the group), and each group is folded into the
+// float32 accumulator with two multiply-adds per element.  MFMA s of a 128-k
+// tile covers k = 32 s .. 32 s + 31 (lane 16 g + r: k = 32 s + 8 g + 0..7), so
+// an MFMA never straddles two groups.  Same block shape, split-K and
+// epilogue as the MX chunk.
+template <bool GATEUP, int KTW>
+__device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act,
+                                                const int32_t* __restrict__ row_token, int g, int row0, int nrows,
+                                                const uint8_t* __restrict__ blob, uint64_t expert_bytes, int H,
+                                                int I, float limit, uint16_t* __restrict__ h_out,
+                                                float* __restrict__ out_rows, f32x4 (*red)[8][64]) {
+  constexpr int KT = kWaves * KTW;
+  constexpr int NT = 8;
+  constexpr int NH = NT / 2;
+  constexpr int G = GATEUP ? 64 : 32;   // group size ("OsaurusAI / DeepSeek-V4-Flash-0731-JANG", recipe)
+  constexpr int NG = 128 / G;           // groups per k tile
+  constexpr int SPG = G / 32;           // MFMAs per group
+  constexpr uint64_t kTileBytes = 512;  // codes of a 16-column x 128-k tile
+  constexpr uint64_t kSbBytes = 16 * NG * 4;
+  constexpr uint64_t kTileStride = static_cast<uint64_t>(KT) * kTileBytes;
+  constexpr uint64_t kSbStride = static_cast<uint64_t>(KT) * kSbBytes;
+  typedef __attribute__((__vector_size__(NG * sizeof(unsigned)))) unsigned u32xg;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kt0 = wave * KTW;
+  const ExpertPlanes pl = expert_planes_a2(H, I);
+  const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
+
+  const uint8_t* nb0;
+  const uint8_t* nb1;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  if (GATEUP) {
+    nb0 = eb + pl.gate_nib + blockIdx.x * NH * kTileStride;
+    nb1 = eb + pl.up_nib + blockIdx.x * NH * kTileStride;
+    sb0 = eb + pl.gate_sc + blockIdx.x * NH * kSbStride;
+    sb1 = eb + pl.up_sc + blockIdx.x * NH * kSbStride;
+  } else {
+    nb0 = eb + pl.down_nib + blockIdx.x * NT * kTileStride;
+    nb1 = nb0 + NH * kTileStride;
+    sb0 = eb + pl.down_sc + blockIdx.x * NT * kSbStride;
+    sb1 = sb0 + NH * kSbStride;
+  }
+  nb0 += static_cast<uint64_t>(kt0) * kTileBytes + lane * 8;
+  nb1 += static_cast<uint64_t>(kt0) * kTileBytes + lane * 8;
+  // the (scale, bias) words of output column lane % 16 (the MFMA result layout)
+  sb0 += static_cast<uint64_t>(kt0) * kSbBytes + (lane & 15) * (NG * 4);
+  sb1 += static_cast<uint64_t>(kt0) * kSbBytes + (lane & 15) * (NG * 4);
+
+  const int r = lane & 15;
+  const int p = row0 + min(r, nrows - 1);
+  const uint16_t* arow = (GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I) +
+                         8 * (lane >> 4) + kt0 * 128;
+
+  // codes two tiles ahead (gate/up: three-deep ring) or one (down, whose
+  // (scale, bias) words take twice the registers: two-deep); activations and
+  // the (scale, bias) words one tile ahead (two-deep rings), issued together
+  constexpr int RB = GATEUP ? 3 : 2;
+  u32x2 bq[RB][NT];
+  u32xg sq[2][NT];
+  u32x4 a[2][4];
+  auto load_b = [&](int buf, int i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      bq[buf][j] = *reinterpret_cast<const u32x2*>((j < NH ? nb0 : nb1) + (j % NH) * kTileStride + i * kTileBytes);
+  };
+  auto load_a = [&](int buf, int i) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[buf][s] = ld16(arow + i * 128 + 32 * s);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      sq[buf][j] = *reinterpret_cast<const u32xg*>((j < NH ? sb0 : sb1) + (j % NH) * kSbStride + i * kSbBytes);
+  };
+
+  const u32x4 ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_a(0, 0);
+  load_b(0, 0);
+  if (KTW > 1) {
+    load_a(1, 1);
+    if (RB == 3) load_b(1, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < KTW; ++i) {
+    if (i + RB - 1 < KTW) load_b((i + RB - 1) % RB, i + RB - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 P[NT];
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);
+      const bool first = (s % SPG) == 0;
+      S = mfma16x16x32(av, ones, first ? f32x4{0.f, 0.f, 0.f, 0.f} : S);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const uint32_t w = bq[i % RB][j][s >> 1];
+        const bf16x8 bv = (s & 1) ? affine2_operand<1>(w) : affine2_operand<0>(w);
+        P[j] = mfma16x16x32(av, bv, first ? f32x4{0.f, 0.f, 0.f, 0.f} : P[j]);
+      }
+      if ((s % SPG) == SPG - 1) {
+        const int gi = s / SPG;  // group within the tile
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const uint32_t sbw = sq[i & 1][j][gi];
+          const float sc = __uint_as_float(sbw << 16);
+          const float bc = fmaf(-4.0f, sc, __uint_as_float(sbw & 0xffff0000u));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(bc, S[e], fmaf(sc, P[j][e], acc[j][e]));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < KTW) load_a(i & 1, i + 2);
+  }
+
+#pragma unroll
+  for (int j = 0; j < NT; ++j) red[wave][j][lane] = acc[j];
+  __syncthreads();
+  auto wave_sum = [&](int j) {
+    f32x4 v = red[0][j][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) v += red[w][j][lane];
+    return v;
+  };
+  const int rbase = 4 * (lane >> 4);
+  if (GATEUP) {
+    for (int jg = wave; jg < NH; jg += kWaves) {
+      const f32x4 gs = wave_sum(jg);
+      const f32x4 us = wave_sum(NH + jg);
+      const int col = blockIdx.x * 16 * NH + jg * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rbase + e;
+        if (rr < nrows) {
+          const float gv = fminf(gs[e], limit);
+          const float uv = fminf(fmaxf(us[e], -limit), limit);
+          h_out[static_cast<size_t>(row0 + rr) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
+        }
+      }
+    }
+  } else {
+    constexpr int kPer = NT / kWaves;
+#pragma unroll
+    for (int jj = 0; jj < kPer; ++jj) {
+      const int j = wave * kPer + jj;
+      const f32x4 os = wave_sum(j);
+      const int col = blockIdx.x * 16 * NT + j * 16 + (lane & 15);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = rbase + e;
+        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = os[e];
+      }
+    }
+  }
+}
+
+constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;  // weight format of the groups a launch covers
+
+// grid (n blocks, nrouted + ceil(T / 16)), 64 * kWaves threads: block row y <
+// nrouted takes the rows of routed expert y (16 at a time; an expert with no
+// rows returns at once), the rest take 16-row chunks of the shared group, so
+// the decode path needs no work list.  nrouted is E, or 0 in a launch of the
+// shared group alone (an MXFP8 shared expert, or the MX shared expert beside
+// 2-bit affine routed experts, whose launch has nrouted = E and no chunks).
+// GATEUP: 64 output columns per block (4 gate + 4 up n-tiles; MXFP8: 32, 2 + 2),
 // K = H, A = x rows via row_token, output h.  Otherwise 128 output columns
-// (8 down n-tiles; W8: 64, 4), K = I, A = h rows, output float32 rows.  Wave
+// (8 down n-tiles; MXFP8: 64, 4), K = I, A = h rows, output float32 rows.  Wave
 // w owns k tiles [w*KTW, (w+1)*KTW) of all the block's n-tiles.  The k loop is
 // fully unrolled over a ring of three register buffers, so two k tiles (8 KB
 // per wave) of weight loads stay in flight while one is consumed; the
 // activation loads of a tile are issued one tile ahead and before the weight
 // loads two tiles ahead, so the in-order load counter never makes a tile wait
 // for a later one.
-template <bool GATEUP, int KTW, bool W8>
+template <bool GATEUP, int KTW, int FMT>
 __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
                                                             const int32_t* __restrict__ row_token,
-                                                            const int32_t* __restrict__ offsets, int E,
+                                                            const int32_t* __restrict__ offsets, int E, int nrouted,
                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
                                                             int H, int I, float limit, uint16_t* __restrict__ h_out,
                                                             float* __restrict__ out_rows) {
-  // blockIdx.y < E: routed expert y, all of its rows (16 at a time);
-  // otherwise chunk y - E of the shared group (16 rows).  W8: chunk y of the
-  // shared group.
   int g, first, end;
-  if (!W8 && static_cast<int>(blockIdx.y) < E) {
+  if (static_cast<int>(blockIdx.y) < nrouted) {
     g = blockIdx.y;
     first = offsets[g];
     end = offsets[g + 1];
   } else {
     g = E;
-    first = offsets[E] + (blockIdx.y - (W8 ? 0 : E)) * kDecodeRows;
+    first = offsets[E] + (blockIdx.y - nrouted) * kDecodeRows;
     end = min(first + kDecodeRows, offsets[E + 1]);
   }
   if (first >= end) return;
   __shared__ f32x4 red[kWaves][8][64];
-  decode_chunk<GATEUP, KTW, W8>(act, row_token, g, first, min(kDecodeRows, end - first), blob, expert_bytes, H, I,
-                                limit, h_out, out_rows, red);
+  auto chunk = [&](int row0, const uint8_t* bl) {
+    if constexpr (FMT == kFmtA2)
+      decode_chunk_a2<GATEUP, KTW>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H, I,
+                                   limit, h_out, out_rows, red);
+    else
+      decode_chunk<GATEUP, KTW, FMT == kFmtMx8>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl,
+                                                expert_bytes, H, I, limit, h_out, out_rows, red);
+  };
+  chunk(first, blob);
   // Experts with more than 16 rows (rare while decoding) take further chunks.
   for (int row0 = first + kDecodeRows; row0 < end; row0 += kDecodeRows) {
     __syncthreads();  // the previous chunk is done with red
@@ -218,8 +408,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
     // of the loop and spill.
     const uint8_t* bl = blob;
     asm volatile("" : "+s"(bl));
-    decode_chunk<GATEUP, KTW, W8>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H, I,
-                                  limit, h_out, out_rows, red);
+    chunk(row0, bl);
   }
 }
 
@@ -227,21 +416,35 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
 
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
                        int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
-                       float* out_rows, bool shared_w8, hipStream_t s) {
+                       float* out_rows, bool shared_w8, bool routed_a2, hipStream_t s) {
   const int K = gateup ? H : I;
   const int ktw = K / (128 * kWaves);  // k tiles per wave; decode_k_ok(K) keeps it in {1, 2, 4, 8}
   if (ktw * 128 * kWaves != K) return;  // never taken: decode_k_ok(K) holds for the decode path
   const int chunks = (T + kDecodeRows - 1) / kDecodeRows;
-  // MXFP4 experts (and the shared one unless it is MXFP8); then the MXFP8 shared expert.
-  dim3 grid(gateup ? I / 64 : H / 128, E + (shared_w8 ? 0 : chunks));
-  dim3 grid8(gateup ? I / 32 : H / 64, chunks);
-#define MOE_DECODE_LAUNCH(G, KTW)                                                                                    \
-  do {                                                                                                             \
-    ffn_decode_kernel<G, KTW, false><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I, limit, \
-                                                                  G ? h : nullptr, G ? nullptr : out_rows);        \
-    if (shared_w8)                                                                                                 \
-      ffn_decode_kernel<G, KTW, true><<<grid8, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, blob, eb, H, I,      \
-                                                                    limit, G ? h : nullptr, G ? nullptr : out_rows); \
+  const int nb = gateup ? I / 64 : H / 128;    // column blocks of the MXFP4 and affine launches
+  const int nb8 = gateup ? I / 32 : H / 64;    // of the MXFP8 launch
+  // Routed experts (MXFP4 or 2-bit affine); the shared group rides along in
+  // the MXFP4 launch, or runs in a launch of its own (MXFP8, or MXFP4 beside
+  // affine routed experts).
+  const bool own_shared = shared_w8 || routed_a2;
+  const dim3 grid(nb, E + (own_shared ? 0 : chunks));
+  const dim3 grid_sh(shared_w8 ? nb8 : nb, chunks);
+  uint16_t* ho = gateup ? h : nullptr;
+  float* oo = gateup ? nullptr : out_rows;
+#define MOE_DECODE_LAUNCH(G, KTW)                                                                                 \
+  do {                                                                                                          \
+    if (routed_a2)                                                                                              \
+      ffn_decode_kernel<G, KTW, kFmtA2><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, E, blob, eb, H, \
+                                                                     I, limit, ho, oo);                         \
+    else                                                                                                        \
+      ffn_decode_kernel<G, KTW, kFmtMx4><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, E, blob, eb,  \
+                                                                      H, I, limit, ho, oo);                     \
+    if (shared_w8)                                                                                              \
+      ffn_decode_kernel<G, KTW, kFmtMx8><<<grid_sh, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, 0, blob,   \
+                                                                         eb, H, I, limit, ho, oo);              \
+    else if (routed_a2)                                                                                         \
+      ffn_decode_kernel<G, KTW, kFmtMx4><<<grid_sh, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, 0, blob,   \
+                                                                         eb, H, I, limit, ho, oo);              \
   } while (0)
 #define MOE_DECODE_SWITCH(G)                     \
   switch (ktw) {                                 \

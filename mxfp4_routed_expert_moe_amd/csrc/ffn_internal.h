@@ -51,16 +51,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K sizes with a compiled decode variant (k tiles per wave: K / 512 with
-// four K-splitting waves, one of 1, 2, 4, 8).
-inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
-
 // Phase 1 (gateup = true: x rows -> h) or phase 2 (h rows -> out_rows).
 // The decode family reads the dispatch offsets directly; the prefill family
 // walks the work list (grid (column blocks, max_items), surplus blocks return).
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
                        int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
-                       float* out_rows, bool shared_w8, hipStream_t s);
+                       float* out_rows, bool shared_w8, bool routed_a2, hipStream_t s);
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
                         int T, int E, bool shared_w8, hipStream_t s);

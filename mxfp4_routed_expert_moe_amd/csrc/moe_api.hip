@@ -22,11 +22,14 @@ int check_experts(const moe_experts* d) {
   if (!d || !d->base) return MOE_EINVAL;
   if (d->abi_version != MOE_ABI_VERSION) return MOE_ELAYOUT;
   if (d->layout != MOE_LAYOUT_GFX950_TILED_V1) return MOE_ELAYOUT;
-  if ((d->flags & ~(MOE_FFN_SPLIT_FP8 | MOE_SHARED_MXFP8)) != 0) return MOE_EINVAL;
-  if ((d->flags & MOE_FFN_SPLIT_FP8) && (d->flags & MOE_SHARED_MXFP8)) return MOE_EINVAL;
+  if ((d->flags & ~(MOE_FFN_SPLIT_FP8 | MOE_SHARED_MXFP8 | MOE_ROUTED_AFFINE2)) != 0) return MOE_EINVAL;
+  if ((d->flags & MOE_FFN_SPLIT_FP8) && (d->flags & (MOE_SHARED_MXFP8 | MOE_ROUTED_AFFINE2))) return MOE_EINVAL;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return MOE_ESHAPE;
-  const uint64_t eb = moe_expert_bytes(d->hidden, d->inter);
+  const bool a2 = (d->flags & MOE_ROUTED_AFFINE2) != 0;
+  const uint64_t eb = a2 ? moe_expert_bytes_affine2(d->hidden, d->inter) : moe_expert_bytes(d->hidden, d->inter);
   if (eb == 0 || d->expert_bytes != eb) return MOE_ESHAPE;
+  // the affine codec runs the decode kernel family at every token count
+  if (a2 && !(moe::decode_k_ok(d->hidden) && moe::decode_k_ok(d->inter))) return MOE_ESHAPE;
   if (!aligned(d->base, 256)) return MOE_EALIGN;
   return MOE_OK;
 }
@@ -114,7 +117,7 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
 size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k) {
   if (T <= 0 || T > kMaxTokens || top_k < 1 || top_k > kMaxTopK || check_experts(experts) != MOE_OK) return 0;
   return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k,
-                           (experts->flags & MOE_FFN_SPLIT_FP8) != 0);
+                           (experts->flags & MOE_FFN_SPLIT_FP8) != 0, (experts->flags & MOE_ROUTED_AFFINE2) != 0);
 }
 
 namespace {
@@ -136,7 +139,8 @@ int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t t
   return hip_status(moe::launch_ffn(x, T, static_cast<const uint8_t*>(experts->base), experts->expert_bytes,
                                     experts->n_experts, experts->hidden, experts->inter, top_k, offsets, row_token,
                                     clamp_limit, out_rows, ws, phase, (experts->flags & MOE_FFN_SPLIT_FP8) != 0,
-                                    (experts->flags & MOE_SHARED_MXFP8) != 0, as_stream(stream)));
+                                    (experts->flags & MOE_SHARED_MXFP8) != 0,
+                                    (experts->flags & MOE_ROUTED_AFFINE2) != 0, as_stream(stream)));
 }
 
 }  // namespace

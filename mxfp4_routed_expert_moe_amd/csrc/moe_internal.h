@@ -95,6 +95,25 @@ __host__ __device__ inline ExpertPlanes expert_planes(int H, int I) {
   return p;
 }
 
+// The planes of a 2-bit affine expert: per projection the code plane (2 bits
+// per weight) then its (scale, bias) plane, 4 bytes per group of 64 (gate,
+// up) or 32 (down) weights.  The *_sc fields point at the (scale, bias) planes.
+__host__ __device__ inline ExpertPlanes expert_planes_a2(int H, int I) {
+  const uint64_t nh = static_cast<uint64_t>(H) * I;
+  ExpertPlanes p;
+  p.gate_nib = 0;
+  p.gate_sc = nh / 4;
+  p.up_nib = nh / 4 + nh / 16;
+  p.up_sc = p.up_nib + nh / 4;
+  p.down_nib = 2 * (nh / 4 + nh / 16);
+  p.down_sc = p.down_nib + nh / 4;
+  return p;
+}
+
+// K sizes with a compiled decode variant of the expert FFN (k tiles per wave:
+// K / 512 with four K-splitting waves, one of 1, 2, 4, 8).
+__host__ __device__ inline bool decode_k_ok(int K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
+
 // Eight E4M3 codes (two 32-bit words, byte order = k order) times one scale
 // -> eight bf16, the B operand of one 16x16x32 bf16 MFMA.  The hardware
 // convert is exact for every code and scale byte < 255 (checked on the
@@ -186,11 +205,12 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* off
                            int32_t* slot_row, void* ws, hipStream_t s);
 
 // split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8);
-// shared_w8: the shared expert is MXFP8 (MOE_SHARED_MXFP8).
-size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8);
+// shared_w8: the shared expert is MXFP8 (MOE_SHARED_MXFP8); routed_a2: the
+// routed experts are 2-bit affine (MOE_ROUTED_AFFINE2: decode family at every T).
+size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool routed_a2);
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
-                      void* ws, int phase, bool split_fp8, bool shared_w8, hipStream_t s);
+                      void* ws, int phase, bool split_fp8, bool shared_w8, bool routed_a2, hipStream_t s);
 
 hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s);

@@ -1,4 +1,5 @@
-// Host repack of MXFP4 expert blobs: canonical layout <-> gfx950 tiled layout.
+// Host repack of expert blobs (MXFP4, MXFP8, 2-bit affine): canonical layout
+// <-> gfx950 tiled layout.
 //
 // Both layouts hold the same six planes (gate, up, down nibbles and scales) at
 // the same offsets; the tiled layout permutes the bytes inside each plane so
@@ -126,6 +127,80 @@ int repack(const uint8_t* src, uint64_t src_bytes, int32_t n_total, int32_t H, i
   return MOE_OK;
 }
 
+// 2-bit affine experts.  Position of canonical code (n, k) of an [N, K]
+// projection in the tiled code plane: byte offset and bit within that byte.
+inline void tiled_code2_pos(int K, int n, int k, uint64_t* byte, int* bit) {
+  const int tile = (n / 16) * (K / 128) + k / 128;
+  const int kk = k % 128;
+  const int s = kk / 32, g = (kk % 32) / 8, i = kk % 8;
+  const int lane = 16 * g + n % 16;
+  const int b = 16 * (i % 2) + 2 * (4 * (s % 2) + i / 2);  // bit in little-endian word s / 2
+  *byte = static_cast<uint64_t>(tile) * 512 + lane * 8 + (s / 2) * 4 + b / 8;
+  *bit = b % 8;
+}
+
+// Offset (from the start of the scale plane) of the 4-byte (scale, bias)
+// entry of row n, group gi in the tiled layout.
+inline uint64_t tiled_sb2_index(int K, int G, int n, int gi) {
+  const int k = gi * G;
+  const uint64_t block = static_cast<uint64_t>(n / 16) * (K / 128) + k / 128;
+  return block * (16 * (128 / G) * 4) + ((n % 16) * (128 / G) + (k % 128) / G) * 4;
+}
+
+void permute_projection2(const uint8_t* src, uint8_t* dst, int N, int K, int G, int dir) {
+  const uint64_t code_bytes = static_cast<uint64_t>(N) * K / 4;
+  memset(dst, 0, code_bytes);
+  for (int n = 0; n < N; ++n) {
+    for (int k = 0; k < K; ++k) {
+      uint64_t tb;
+      int bit;
+      tiled_code2_pos(K, n, k, &tb, &bit);
+      const uint64_t cb = static_cast<uint64_t>(n) * (K / 4) + k / 4;
+      const int cbit = 2 * (k % 4);
+      if (dir > 0) dst[tb] |= static_cast<uint8_t>(((src[cb] >> cbit) & 3) << bit);
+      else dst[cb] |= static_cast<uint8_t>(((src[tb] >> bit) & 3) << cbit);
+    }
+  }
+  const uint64_t ng = static_cast<uint64_t>(N) * (K / G);  // groups; canonical scales then biases, 2 bytes each
+  const uint8_t* s_sb = src + code_bytes;
+  uint8_t* d_sb = dst + code_bytes;
+  for (int n = 0; n < N; ++n) {
+    for (int gi = 0; gi < K / G; ++gi) {
+      const uint64_t c = static_cast<uint64_t>(n) * (K / G) + gi;
+      const uint64_t t = tiled_sb2_index(K, G, n, gi);
+      if (dir > 0) {
+        memcpy(d_sb + t, s_sb + 2 * c, 2);
+        memcpy(d_sb + t + 2, s_sb + 2 * ng + 2 * c, 2);
+      } else {
+        memcpy(d_sb + 2 * c, s_sb + t, 2);
+        memcpy(d_sb + 2 * ng + 2 * c, s_sb + t + 2, 2);
+      }
+    }
+  }
+}
+
+int repack2(const uint8_t* src, uint64_t src_bytes, int32_t n_experts, int32_t H, int32_t I, uint8_t* dst,
+            uint64_t dst_bytes, int dir) {
+  if (!src || !dst) return MOE_EINVAL;
+  if (n_experts <= 0) return MOE_EINVAL;
+  if (!shape_ok(H, I)) return MOE_ESHAPE;
+  const uint64_t eb = moe_expert_bytes_affine2(H, I);
+  const uint64_t need = eb * static_cast<uint64_t>(n_experts);
+  if (src_bytes < need || dst_bytes < need) return MOE_EINVAL;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + need && b < a + need) return MOE_EINVAL;  // overlapping buffers
+  const uint64_t nh = static_cast<uint64_t>(H) * I;
+  const uint64_t pg = nh / 4 + 4 * (nh / 64);  // gate (and up) projection bytes
+  for (int32_t x = 0; x < n_experts; ++x) {
+    const uint8_t* s = src + eb * x;
+    uint8_t* d = dst + eb * x;
+    permute_projection2(s, d, I, H, 64, dir);                    // gate [I, H], groups of 64
+    permute_projection2(s + pg, d + pg, I, H, 64, dir);          // up   [I, H], groups of 64
+    permute_projection2(s + 2 * pg, d + 2 * pg, H, I, 32, dir);  // down [H, I], groups of 32
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +233,21 @@ int moe_pack_mxfp8(const uint8_t* src_canonical, uint64_t src_bytes, int32_t hid
 int moe_unpack_mxfp8(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t hidden, int32_t inter,
                      uint8_t* dst_canonical, uint64_t dst_bytes) {
   return repack8(src_device_layout, src_bytes, hidden, inter, dst_canonical, dst_bytes, -1);
+}
+
+uint64_t moe_expert_bytes_affine2(int32_t hidden, int32_t inter) {
+  if (!shape_ok(hidden, inter)) return 0;
+  return static_cast<uint64_t>(hidden) * static_cast<uint64_t>(inter);
+}
+
+int moe_pack_affine2(const uint8_t* src_canonical, uint64_t src_bytes, int32_t n_experts, int32_t hidden,
+                     int32_t inter, uint8_t* dst_device_layout, uint64_t dst_bytes) {
+  return repack2(src_canonical, src_bytes, n_experts, hidden, inter, dst_device_layout, dst_bytes, +1);
+}
+
+int moe_unpack_affine2(const uint8_t* src_device_layout, uint64_t src_bytes, int32_t n_experts, int32_t hidden,
+                       int32_t inter, uint8_t* dst_canonical, uint64_t dst_bytes) {
+  return repack2(src_device_layout, src_bytes, n_experts, hidden, inter, dst_canonical, dst_bytes, -1);
 }
 
 }  // extern "C"

@@ -89,11 +89,13 @@ def check_dispatch(g, ids_gpu, E):
     return off, rt, sr
 
 
-def full_check(inp: WL.LayerInputs, experts: B.Experts, sample_tokens=None, seed=0, shared_fmt="mxfp4"):
+def full_check(inp: WL.LayerInputs, experts: B.Experts, sample_tokens=None, seed=0, shared_fmt="mxfp4",
+               routed_fmt="mxfp4"):
     """Whole-layer parity: routing, dispatch, expert rows and y.  With
     sample_tokens, the expert rows and outputs are checked on that many
     randomly chosen tokens (the oracle computes each one on its own).
-    shared_fmt: the shared expert's weight format in inp.experts."""
+    shared_fmt, routed_fmt: the weight formats of the shared and the routed
+    experts in inp.experts."""
     g = run_gpu_layer(inp, experts)
     ids_ref, w_ref, gap = oracle_routing(inp)
     n_amb = check_routing(g, ids_ref, w_ref, gap)
@@ -112,8 +114,8 @@ def full_check(inp: WL.LayerInputs, experts: B.Experts, sample_tokens=None, seed
     ref_rows = {}
     grp = np.searchsorted(off, rows, side="right") - 1
     for e in np.unique(grp):
-        fmt = shared_fmt if int(e) == inp.n_experts else "mxfp4"
-        mats = O.decode_expert(inp.experts, int(e), inp.hidden, inp.inter, fmt)
+        fmt = shared_fmt if int(e) == inp.n_experts else routed_fmt
+        mats = O.decode_expert(inp.experts, int(e), inp.hidden, inp.inter, fmt, routed_fmt)
         rs = rows[grp == e]
         o = O.expert_forward(xf[rt[rs]], mats, WL.CLAMP_LIMIT)
         for r, v in zip(rs, o):

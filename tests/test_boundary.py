@@ -119,6 +119,54 @@ def test_pack_mxfp8_matches_documented_layout_and_round_trips(shape):
     assert L.moe_expert_bytes_mxfp8(4096, 2048) == 25_952_256 and L.moe_expert_bytes_mxfp8(4000, 2048) == 0
 
 
+def _spec_affine2_code(packed, base, N, K, n, k):
+    """Canonical 2-bit code (n, k) read from the device layout as include/moe.h
+    describes it (512-byte tiles; lane 16g + r; word s // 2; the code of (s, i)
+    at bit 16 (i % 2) + 2 (4 (s % 2) + i // 2))."""
+    tile = (n // 16) * (K // 128) + k // 128
+    kk = k % 128
+    s_, g, i = kk // 32, (kk % 32) // 8, kk % 8
+    word = base + tile * 512 + (16 * g + n % 16) * 8 + 4 * (s_ // 2)
+    w = int.from_bytes(bytes(packed[word:word + 4]), "little")
+    return (w >> (16 * (i % 2) + 2 * (4 * (s_ % 2) + i // 2))) & 3
+
+
+@pytest.mark.parametrize("shape", [(512, 512), (1024, 512), (512, 2048)])
+def test_pack_affine2_matches_documented_layout_and_round_trips(shape):
+    H, I = shape
+    E = 2
+    canon = WL.make_experts_affine2(11, E, H, I)[:E * H * I]
+    assert B.lib().moe_expert_bytes_affine2(H, I) == H * I == WL.affine2_expert_bytes(H, I)
+    packed = B.pack_affine2(canon, E, H, I)
+    assert not np.array_equal(packed, canon)
+    assert np.array_equal(B.unpack_affine2(packed, E, H, I), canon)
+    g = np.random.default_rng(2)
+    for x in range(E):
+        base = x * H * I
+        for (N, K), G in zip(((I, H), (I, H), (H, I)), (64, 64, 32)):
+            for _ in range(200):
+                n, k = int(g.integers(N)), int(g.integers(K))
+                want = (int(canon[base + n * (K // 4) + k // 4]) >> (2 * (k % 4))) & 3
+                assert _spec_affine2_code(packed, base, N, K, n, k) == want
+                # (scale, bias) of (n, k): 16 * (128 / G) * 4-byte blocks, entry (n % 16) * (128 / G) + (k % 128) / G
+                sb = base + N * K // 4
+                blk = (n // 16) * (K // 128) + k // 128
+                at = sb + blk * 16 * (128 // G) * 4 + ((n % 16) * (128 // G) + (k % 128) // G) * 4
+                ng = N * K // G
+                ci = n * (K // G) + k // G
+                assert bytes(packed[at:at + 2]) == bytes(canon[sb + 2 * ci: sb + 2 * ci + 2])              # scale
+                assert bytes(packed[at + 2:at + 4]) == bytes(canon[sb + 2 * ng + 2 * ci: sb + 2 * ng + 2 * ci + 2])
+            base += N * K // 4 + 4 * (N * K // G)
+    L = B.lib()
+    n = canon.nbytes
+    out = np.empty_like(canon)
+    assert L.moe_pack_affine2(canon.ctypes.data, n - 1, E, H, I, out.ctypes.data, n) == EINVAL
+    assert L.moe_pack_affine2(canon.ctypes.data, n, E, H, I + 1, out.ctypes.data, n) == ESHAPE
+    assert L.moe_pack_affine2(canon.ctypes.data, n, 0, H, I, out.ctypes.data, n) == EINVAL
+    assert L.moe_pack_affine2(canon.ctypes.data, n, E, H, I, canon.ctypes.data + 16, n) == EINVAL  # overlap
+    assert L.moe_expert_bytes_affine2(4096, 2048) == 8_388_608 and L.moe_expert_bytes_affine2(4000, 2048) == 0
+
+
 def test_pack_rejects_bad_arguments():
     L = B.lib()
     a = np.zeros(B.expert_bytes(512, 512) * 2, dtype=np.uint8)
@@ -216,11 +264,25 @@ def test_ffn_checks():
     assert _ffn(d=_desc(expert_bytes=13_369_344 + 32)) == ESHAPE
     assert _ffn(d=_desc(hidden=4000)) == ESHAPE
     assert _ffn(d=_desc(n_experts=0)) == ESHAPE
-    assert _ffn(d=_desc(flags=4)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
+    assert _ffn(d=_desc(flags=8)) == EINVAL and _ffn(d=_desc(flags=-1)) == EINVAL   # unknown flag bits
     assert _ffn(T=B.MOE_MAX_TOKENS + 1) == ESHAPE
     assert B.lib().moe_ffn_workspace_size(B.MOE_MAX_TOKENS + 1, ctypes.byref(_desc()), 6) == 0
     assert _ffn(d=_desc(flags=B.MOE_FFN_SPLIT_FP8 | B.MOE_SHARED_MXFP8)) == EINVAL  # not combinable
     assert _ffn(d=_desc(flags=B.MOE_SHARED_MXFP8), T=0) == OK
+    # 2-bit affine routed experts: expert_bytes = H * I, decode-family K sizes only, no split option
+    a2 = dict(flags=B.MOE_ROUTED_AFFINE2, expert_bytes=4096 * 2048)
+    assert _ffn(d=_desc(**a2), T=0) == OK
+    assert _ffn(d=_desc(flags=B.MOE_ROUTED_AFFINE2)) == ESHAPE                          # MXFP4 expert_bytes
+    assert _ffn(d=_desc(**dict(a2, flags=B.MOE_ROUTED_AFFINE2 | B.MOE_SHARED_MXFP8)), T=0) == OK
+    assert _ffn(d=_desc(**dict(a2, flags=B.MOE_ROUTED_AFFINE2 | B.MOE_FFN_SPLIT_FP8))) == EINVAL
+    assert _ffn(d=_desc(flags=B.MOE_ROUTED_AFFINE2, hidden=1536, expert_bytes=1536 * 2048)) == ESHAPE
+    d_ok = _desc(flags=B.MOE_ROUTED_AFFINE2, hidden=1536, expert_bytes=1536 * 2048)
+    d_ok.flags = 0
+    d_ok.expert_bytes = B.lib().moe_expert_bytes(1536, 2048)
+    assert _ffn(d=d_ok, T=0) == OK                      # the same shape is fine for MXFP4 (prefill family)
+    # the affine codec takes the decode family at every T: its workspace has no split planes, h is bf16
+    wa2 = B.lib().moe_ffn_workspace_size(4096, ctypes.byref(_desc(**a2)), 6)
+    assert wa2 >= 7 * 4096 * 2048 * 2 and wa2 < 7 * 4096 * 2048 * 2 + 7 * 4096 * 16 // 16 * 16 + (1 << 20)
     assert _ffn(d=_desc(base=FAKE + 128)) == EALIGN
     assert _ffn(d=_desc(base=None)) == EINVAL
     assert _ffn(k=0) == ESHAPE and _ffn(k=9) == ESHAPE

@@ -478,3 +478,70 @@ def test_shared_mxfp8_full_workloads(index, sample):
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r, ex
     torch.cuda.empty_cache()
+
+
+# The routed experts in the 2-bit affine codec (MOE_ROUTED_AFFINE2): the
+# decode kernel family at every T, the shared expert in its own MX launch.
+def _affine2_inputs(T, H, I, E, seed, routing="learned", shared="mxfp4"):
+    inp = _small_inputs(T, H, I, E, seed, routing)
+    inp.experts = WL.make_experts_affine2(seed, E, H, I, shared)
+    return inp
+
+
+@pytest.mark.parametrize("T,H,I,E,routing,shared", [
+    (5, 512, 1024, 16, "learned", "mxfp4"),     # one chunk per group
+    (37, 512, 512, 16, "learned", "mxfp4"),     # routed groups and the shared group over 16 rows: several chunks
+    (61, 1024, 512, 64, "hash", "mxfp4"),       # hash routing; gate/up K = 1024
+    (300, 512, 512, 16, "learned", "mxfp4"),    # a prefill-sized T on the decode family (~112 rows per expert)
+    (200, 1024, 2048, 32, "learned", "mxfp4"),  # down K = 2048 (four k tiles per wave, two-deep code ring)
+    (37, 512, 512, 16, "learned", "mxfp8"),     # with the MXFP8 shared expert (the recipe's 8-bit shared expert)
+    (9, 4096, 512, 16, "learned", "mxfp8"),     # gate/up K = 4096 (eight k tiles per wave)
+])
+def test_affine2_small_shapes(T, H, I, E, routing, shared):
+    print(f"[parity] affine2 T={T} H={H} I={I} E={E} {routing} shared {shared}", flush=True)
+    inp = _affine2_inputs(T, H, I, E, 2000 + T, routing, shared)
+    ex = B.Experts.from_canonical(inp.experts, E, H, I, shared_mxfp8=shared == "mxfp8", routed_affine2=True)
+    r = LC.full_check(inp, ex, shared_fmt=shared, routed_fmt="affine2")
+    assert r["ambiguous"] == 0
+    g = r["g"]
+    ref = O.moe_layer(inp.x, inp.experts, n_experts=E, hidden=H, inter=I, top_k=6, route_scale=1.5,
+                      limit=WL.CLAMP_LIMIT, w_router=inp.router, bias=inp.bias, token_ids=inp.tok, table=inp.table,
+                      shared_fmt=shared, routed_fmt="affine2")
+    n = int(ref["offsets"][-1])
+    LC.assert_output_close(LC.host(g["out_rows"][:n]), ref["out_rows"], "all rows")
+    LC.assert_output_close(O.bf16_bits_to_f64(g["y"]), ref["y"], "all outputs")
+    print(f"[parity] affine2 T={T}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}", flush=True)
+
+
+def test_affine2_deterministic_and_phases():
+    # two runs bit-identical; the three FFN phases one at a time equal one call
+    T, H, I, E = 37, 512, 512, 16
+    inp = _affine2_inputs(T, H, I, E, 77)
+    ex = B.Experts.from_canonical(inp.experts, E, H, I, routed_affine2=True)
+    a = LC.run_gpu_layer(inp, ex)
+    b = LC.run_gpu_layer(inp, ex)
+    n = int(a["offsets"][-1])
+    assert torch.equal(a["out_rows"][:n], b["out_rows"][:n]) and np.array_equal(a["y"], b["y"])
+    layer = a["layer"]
+    ref = layer.out_rows.clone()
+    layer.out_rows.zero_()
+    xd = LC.dev(inp.x)
+    for ph in (0, 1, 2):
+        layer.expert_ffn_phase(xd, ph)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.out_rows[:n], ref[:n])
+
+
+@pytest.mark.parametrize("index,sample", [(0, 4), (1, 10), (2, 8), (3, 6)])
+def test_affine2_full_workloads(index, sample):
+    w = WL.WORKLOADS[index]
+    print(f"[parity] affine2 full workload {w.name} T={w.T}", flush=True)
+    _EXPERTS_CACHE.clear()
+    canon = WL.make_experts_affine2(w.seed, WL.N_EXPERTS)
+    inp = WL.make_layer_inputs(w, experts=canon)
+    ex = B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, routed_affine2=True)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, routed_fmt="affine2")
+    print(f"[parity] affine2 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
+    del r, ex
+    torch.cuda.empty_cache()

@@ -47,6 +47,8 @@ def _parse():
     p.add_argument("--ffn-split-fp8", action="store_true",
                    help="prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8)")
     p.add_argument("--shared-mxfp8", action="store_true", help="the shared expert in MXFP8 (MOE_SHARED_MXFP8)")
+    p.add_argument("--routed-affine2", action="store_true",
+                   help="the routed experts in the 2-bit affine codec (MOE_ROUTED_AFFINE2)")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="run one device copy of this size first (to scale HBM counters)")
     return p.parse_args()
@@ -78,7 +80,7 @@ def read_traffic(workload: str, source: str):
         return None
 
 
-def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4"):
+def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4", routed_fmt: str = "mxfp4"):
     """The oracle as it stands, on the first n_tokens of the workload."""
     import numpy as np
     from oracle import moe_oracle as O
@@ -93,7 +95,7 @@ def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4"):
     r = O.moe_layer(inp.x[:S], inp.experts, n_experts=inp.n_experts, hidden=inp.hidden, inter=inp.inter,
                     top_k=inp.top_k, route_scale=WL.ROUTE_SCALE, limit=WL.CLAMP_LIMIT, w_router=inp.router,
                     bias=inp.bias, token_ids=None if inp.tok is None else inp.tok[:S], table=inp.table,
-                    shared_fmt=shared_fmt)
+                    shared_fmt=shared_fmt, routed_fmt=routed_fmt)
     dt = time.perf_counter() - t0
     n_exp = int(np.count_nonzero(np.diff(r["offsets"])))
     return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle",
@@ -119,11 +121,19 @@ def main():
     B.lib()  # fail loudly if the library is missing
     wl = {w.name: w for w in WL.WORKLOADS}[args.workload]
     print(f"[bench] workload {wl.name} T={wl.T}: generating inputs", file=sys.stderr, flush=True)
-    if args.shared_mxfp8 and args.ffn_split_fp8:
-        print("--shared-mxfp8 and --ffn-split-fp8 do not combine", file=sys.stderr)
+    if args.ffn_split_fp8 and (args.shared_mxfp8 or args.routed_affine2):
+        print("--ffn-split-fp8 combines with neither --shared-mxfp8 nor --routed-affine2", file=sys.stderr)
         sys.exit(2)
-    inp = WL.make_layer_inputs(wl, experts=WL.make_experts_shared_mxfp8(wl.seed, WL.N_EXPERTS)
-                               if args.shared_mxfp8 else None)
+    shared_fmt = "mxfp8" if args.shared_mxfp8 else "mxfp4"
+    routed_fmt = "affine2" if args.routed_affine2 else "mxfp4"
+    if args.routed_affine2:
+        canon = WL.make_experts_affine2(wl.seed, WL.N_EXPERTS, shared=shared_fmt)
+    elif args.shared_mxfp8:
+        canon = WL.make_experts_shared_mxfp8(wl.seed, WL.N_EXPERTS)
+    else:
+        canon = None
+    inp = WL.make_layer_inputs(wl, experts=canon)
+    del canon
     H, I, E, k, T = inp.hidden, inp.inter, inp.n_experts, inp.top_k, wl.T
 
     dev = torch.device("cuda", 0)
@@ -137,15 +147,17 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    if args.shared_mxfp8:
-        nb = E * WL.expert_bytes(H, I)
-        packed = np.concatenate([B.pack_mxfp4(inp.experts[:nb], E, H, I), B.pack_mxfp8(inp.experts[nb:], H, I)])
-    else:
-        packed = B.pack_mxfp4(inp.experts, E + 1, H, I)
+    nb = E * (WL.affine2_expert_bytes(H, I) if args.routed_affine2 else WL.expert_bytes(H, I))
+    routed = (B.pack_affine2(inp.experts[:nb], E, H, I) if args.routed_affine2
+              else B.pack_mxfp4(inp.experts[:nb], E, H, I))
+    shared = B.pack_mxfp8(inp.experts[nb:], H, I) if args.shared_mxfp8 else B.pack_mxfp4(inp.experts[nb:], 1, H, I)
+    packed = np.concatenate([routed, shared])
+    del routed, shared
     blob0 = torch.from_numpy(packed).to(dev)
     del packed
     blobs = [blob0] + [blob0.clone() for _ in range(args.copies - 1)]
-    experts = [B.Experts(b, E, H, I, split_fp8=args.ffn_split_fp8, shared_mxfp8=args.shared_mxfp8) for b in blobs]
+    experts = [B.Experts(b, E, H, I, split_fp8=args.ffn_split_fp8, shared_mxfp8=args.shared_mxfp8,
+                         routed_affine2=args.routed_affine2) for b in blobs]
     to_dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     layer = B.MoeLayer(experts[0], T, k, WL.ROUTE_SCALE, WL.CLAMP_LIMIT, w_router=to_dev(inp.router),
                        sel_bias=to_dev(inp.bias), hash_table=to_dev(inp.table))
@@ -190,11 +202,16 @@ def main():
     ids = layer.ids.cpu().numpy()
     used = int(len(np.unique(ids[(ids >= 0) & (ids < E)]))) + 1   # + the shared expert
     rows = int(layer.offsets[-1].item())
-    proj_bytes = H * I * 17 // 32
-    shared_proj = H * I * 33 // 32 if args.shared_mxfp8 else proj_bytes  # the shared expert's projection bytes
-    gateup_bytes = (used - 1) * 2 * proj_bytes + 2 * shared_proj + rows * H * 2 + rows * I * 2
+    # expert bytes per projection: routed gate / up and down, and the shared expert's
+    mx4_proj = H * I * 17 // 32
+    if args.routed_affine2:
+        gate_proj, down_proj = H * I * 5 // 16, H * I * 3 // 8    # 2 bits + bf16 (s, b) per 64 / per 32
+    else:
+        gate_proj = down_proj = mx4_proj
+    shared_proj = H * I * 33 // 32 if args.shared_mxfp8 else mx4_proj
+    gateup_bytes = (used - 1) * 2 * gate_proj + 2 * shared_proj + rows * H * 2 + rows * I * 2
     gateup_flops = rows * 2 * 2 * H * I
-    decode = rows <= 16 * (E + 1)
+    decode = rows <= 16 * (E + 1) or args.routed_affine2   # the affine codec runs the decode family at every T
     if decode:
         achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -213,13 +230,14 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / FP8_MFMA_PEAK_TFLOPS, 4), issued_tflops=round(2 * achieved, 1))
         traffic = read_traffic(wl.name, "ffn_prefill_f8.hip")
-    roof["traffic"] = traffic
+    # the counter summaries were taken on the MXFP4 experts with an MXFP4 shared expert
+    roof["traffic"] = None if (args.routed_affine2 or args.shared_mxfp8) else traffic
     roof["kernel"] = "ffn gate/up (moe_expert_ffn phase 1)"
     roof["avg_launch_us"] = round(gateup_ms * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = gateup_bytes
     roof["algorithmic_flops_per_launch"] = gateup_flops
 
-    layer_bytes = (used - 1) * 3 * proj_bytes + 3 * shared_proj
+    layer_bytes = (used - 1) * (2 * gate_proj + down_proj) + 3 * shared_proj
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -234,11 +252,13 @@ def main():
         "dtype": "fp8x2-fp4" if (args.ffn_split_fp8 and not decode) else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
-                   "routing": wl.routing, "bias": wl.bias, "weights": "mxfp4 e2m1+e8m0/32",
+                   "routing": wl.routing, "bias": wl.bias,
+                   "weights": ("affine 2-bit, bf16 (s, b) per 64/64/32" if args.routed_affine2
+                               else "mxfp4 e2m1+e8m0/32"),
                    "experts_read_per_step": used, "expert_bytes_per_step": layer_bytes,
                    "blob_copies_rotated": len(experts),
                    "ffn_prefill_arith": "split-fp8 scaled mfma" if args.ffn_split_fp8 else "bf16 mfma",
-                   "shared_expert": "mxfp8" if args.shared_mxfp8 else "mxfp4"},
+                   "shared_expert": shared_fmt},
         "roofline": roof,
         "layer_hbm_gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "stages_us": {"ffn_gateup": round(gateup_ms * 1e3, 2), "ffn_down": round(down_ms * 1e3, 2)},
@@ -246,7 +266,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens, "mxfp8" if args.shared_mxfp8 else "mxfp4")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens, shared_fmt, routed_fmt)
     print(json.dumps(out), flush=True)
 
 

@@ -159,13 +159,14 @@ uint32_t moe_abi_version(void);
  *     lane l = 16*g + r owns bytes [8l, 8l+8) as two little-endian words; word
  *     u holds the 16 codes of row 16*(n/16) + r at columns 128*(k/128) +
  *     32*s + 8*g + i for s in {2u, 2u+1}, i < 8, code (s, i) in bits
- *     16*(i%2) + 2*(4*(s%2) + i/2) +1 : +0.
+ *     4*i + 2*(s%2) +1 : +0 (so word & 0x33333333 and (word >> 2) &
+ *     0x33333333 are eight E2M1 nibbles each, code q read as the value q/2).
  *   scale and bias planes, together: blocks of 16 * (128/G) * 4 bytes, block
  *     (n/16) * (K/128) + (k/128); entry (n%16) * (128/G) + (k%128)/G of a
  *     block is 4 bytes: the bf16 scale, then the bf16 bias, of row n's group
  *     at column k.
  * So one 8-byte load per lane gives a wave the codes of a 16-column x 128-k
- * tile, each group of 8 codes feeding one 16x16x32 MFMA over a single group.
+ * tile, each run of 8 codes feeding one 16x16x32 MFMA inside a single group.
  */
 typedef struct moe_experts {
   uint32_t abi_version;   /* MOE_ABI_VERSION */
@@ -293,7 +294,8 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
  * in experts->flags and a prefill-sized T, fed as stored to the scaled FP4
  * matrix cores); only the experts that own rows are read.  With
  * MOE_ROUTED_AFFINE2 each routed projection is computed per group as
- * s * (x . q) + b * sum(x) (the same sum, regrouped), x . q on bf16 MFMA.
+ * s * (x . q) + b * sum(x) (the same sum, regrouped), x . q and sum(x) on bf16
+ * MFMA.
  *
  * x         bf16 [T, H]; experts: descriptor (host pointer) of the device blob
  * offsets, row_token: as written by moe_dispatch for the same T, E, top_k

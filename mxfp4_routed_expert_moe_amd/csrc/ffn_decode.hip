@@ -173,30 +173,25 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
 }
 
 // 2-bit affine codes -> MFMA B operand.  Word w of a tile lane holds the
-// codes of two MFMAs (half = s % 2); pair p of MFMA s sits at bits 2*sigma
-// (even k) and 16 + 2*sigma (odd k), sigma = 4 * half + p.  Shifted to bits
-// 5..6 of each 16-bit half under the bf16 pattern 0x4080 (4.0), a code q
-// becomes the bf16 value 4 + q exactly: eight values 4 + q in k order.
+// codes of two MFMAs: code i of MFMA s sits in bits 4i + 2(s%2) + 1 : +0, so
+// w & 0x33333333 (s even) or (w >> 2) & 0x33333333 (s odd) is eight E2M1
+// nibbles 00qq, which encode q / 2; the scaled convert with scale 2 turns them
+// into the eight bf16 values q, exactly.
 template <int HALF>
 __device__ __forceinline__ bf16x8 affine2_operand(uint32_t w) {
-  u32x4 o;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    constexpr int kBase = 2 * 4 * HALF - 5;
-    const int sh = kBase + 2 * p;
-    const uint32_t t = sh >= 0 ? (w >> sh) : (w << -sh);
-    o[p] = (t & 0x00600060u) | 0x40804080u;
-  }
-  return __builtin_bit_cast(bf16x8, o);
+  const uint32_t nib = (HALF ? (w >> 2) : w) & 0x33333333u;
+  return dequant8(nib, e8m0_scale_operand(128u));
 }
 
 // One chunk of at most 16 rows of 2-bit affine routed expert g.  Per group of
 // G input columns (64 for gate and up, 32 for down), with q the codes and s, b
 // the group's bf16 scale and bias,
-//   sum_k x_k (s q_k + b) = s * (sum_k x_k (4 + q_k)) + (b - 4 s) * sum_k x_k,
-// so the MFMAs run x against the exact bf16 values 4 + q (P) and against ones
-// (S, the row sums of x over the group), and each group is folded into the
-// float32 accumulator with two multiply-adds per element.  MFMA s of a 128-k
+//   sum_k x_k (s q_k + b) = s * (sum_k x_k q_k) + b * sum_k x_k,
+// so the MFMAs run x against the exact bf16 values q (P) and against ones (S,
+// the row sums of x over the group), and each group is folded into the
+// float32 accumulator with two multiply-adds per element.  (The bias term as
+// MFMAs of x against the broadcast bias, instead of S and a multiply-add,
+// measured slower: the matrix cores are as busy as the vector unit here.)  MFMA s of a 128-k
 // tile covers k = 32 s .. 32 s + 31 (lane 16 g + r: k = 32 s + 8 g + 0..7), so
 // an MFMA never straddles two groups.  Same block shape, split-K and
 // epilogue as the MX chunk.
@@ -285,29 +280,29 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
   for (int i = 0; i < KTW; ++i) {
     if (i + RB - 1 < KTW) load_b((i + RB - 1) % RB, i + RB - 1);
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 P[NT];
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    // group by group: its row sums S, then per n-tile the group's MFMAs into
+    // a fresh P and the fold, so one P is live at a time
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);
-      const bool first = (s % SPG) == 0;
-      S = mfma16x16x32(av, ones, first ? f32x4{0.f, 0.f, 0.f, 0.f} : S);
+    for (int gi = 0; gi < NG; ++gi) {
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ss = 0; ss < SPG; ++ss)
+        S = mfma16x16x32(__builtin_bit_cast(bf16x8, a[i & 1][gi * SPG + ss]), ones, S);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const uint32_t w = bq[i % RB][j][s >> 1];
-        const bf16x8 bv = (s & 1) ? affine2_operand<1>(w) : affine2_operand<0>(w);
-        P[j] = mfma16x16x32(av, bv, first ? f32x4{0.f, 0.f, 0.f, 0.f} : P[j]);
-      }
-      if ((s % SPG) == SPG - 1) {
-        const int gi = s / SPG;  // group within the tile
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const uint32_t sbw = sq[i & 1][j][gi];
-          const float sc = __uint_as_float(sbw << 16);
-          const float bc = fmaf(-4.0f, sc, __uint_as_float(sbw & 0xffff0000u));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(bc, S[e], fmaf(sc, P[j][e], acc[j][e]));
+        for (int ss = 0; ss < SPG; ++ss) {
+          const int s = gi * SPG + ss;
+          const uint32_t w = bq[i % RB][j][s >> 1];
+          const bf16x8 bv = (s & 1) ? affine2_operand<1>(w) : affine2_operand<0>(w);
+          P = mfma16x16x32(__builtin_bit_cast(bf16x8, a[i & 1][s]), bv, P);
         }
+        const uint32_t sbw = sq[i & 1][j][gi];
+        const float sc = __uint_as_float(sbw << 16);          // bf16 scale (low half)
+        const float bc = __uint_as_float(sbw & 0xffff0000u);  // bf16 bias (high half)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(bc, S[e], fmaf(sc, P[e], acc[j][e]));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -361,8 +356,9 @@ constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;  // weight format of the gro
 // nrouted takes the rows of routed expert y (16 at a time; an expert with no
 // rows returns at once), the rest take 16-row chunks of the shared group, so
 // the decode path needs no work list.  nrouted is E, or 0 in a launch of the
-// shared group alone (an MXFP8 shared expert, or the MX shared expert beside
-// 2-bit affine routed experts, whose launch has nrouted = E and no chunks).
+// shared group alone (an MXFP8 shared expert, whose other launch then has no
+// chunks).  Beside 2-bit affine routed experts an MXFP4 shared expert rides in
+// the affine launch (its blocks take the MXFP4 chunk code).
 // GATEUP: 64 output columns per block (4 gate + 4 up n-tiles; MXFP8: 32, 2 + 2),
 // K = H, A = x rows via row_token, output h.  Otherwise 128 output columns
 // (8 down n-tiles; MXFP8: 64, 4), K = I, A = h rows, output float32 rows.  Wave
@@ -392,10 +388,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
   if (first >= end) return;
   __shared__ f32x4 red[kWaves][8][64];
   auto chunk = [&](int row0, const uint8_t* bl) {
-    if constexpr (FMT == kFmtA2)
-      decode_chunk_a2<GATEUP, KTW>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H, I,
-                                   limit, h_out, out_rows, red);
-    else
+    if constexpr (FMT == kFmtA2) {
+      if (g < E)
+        decode_chunk_a2<GATEUP, KTW>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H, I,
+                                     limit, h_out, out_rows, red);
+      else  // the MXFP4 shared expert beside affine routed experts
+        decode_chunk<GATEUP, KTW, false>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H,
+                                         I, limit, h_out, out_rows, red);
+    } else
       decode_chunk<GATEUP, KTW, FMT == kFmtMx8>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl,
                                                 expert_bytes, H, I, limit, h_out, out_rows, red);
   };
@@ -423,12 +423,10 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
   const int chunks = (T + kDecodeRows - 1) / kDecodeRows;
   const int nb = gateup ? I / 64 : H / 128;    // column blocks of the MXFP4 and affine launches
   const int nb8 = gateup ? I / 32 : H / 64;    // of the MXFP8 launch
-  // Routed experts (MXFP4 or 2-bit affine); the shared group rides along in
-  // the MXFP4 launch, or runs in a launch of its own (MXFP8, or MXFP4 beside
-  // affine routed experts).
-  const bool own_shared = shared_w8 || routed_a2;
-  const dim3 grid(nb, E + (own_shared ? 0 : chunks));
-  const dim3 grid_sh(shared_w8 ? nb8 : nb, chunks);
+  // Routed experts (MXFP4 or 2-bit affine); an MXFP4 shared group rides along
+  // in the same launch, an MXFP8 one runs in a launch of its own.
+  const dim3 grid(nb, E + (shared_w8 ? 0 : chunks));
+  const dim3 grid_sh(nb8, chunks);
   uint16_t* ho = gateup ? h : nullptr;
   float* oo = gateup ? nullptr : out_rows;
 #define MOE_DECODE_LAUNCH(G, KTW)                                                                                 \
@@ -441,9 +439,6 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
                                                                       H, I, limit, ho, oo);                     \
     if (shared_w8)                                                                                              \
       ffn_decode_kernel<G, KTW, kFmtMx8><<<grid_sh, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, 0, blob,   \
-                                                                         eb, H, I, limit, ho, oo);              \
-    else if (routed_a2)                                                                                         \
-      ffn_decode_kernel<G, KTW, kFmtMx4><<<grid_sh, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, 0, blob,   \
                                                                          eb, H, I, limit, ho, oo);              \
   } while (0)
 #define MOE_DECODE_SWITCH(G)                     \

@@ -134,7 +134,7 @@ inline void tiled_code2_pos(int K, int n, int k, uint64_t* byte, int* bit) {
   const int kk = k % 128;
   const int s = kk / 32, g = (kk % 32) / 8, i = kk % 8;
   const int lane = 16 * g + n % 16;
-  const int b = 16 * (i % 2) + 2 * (4 * (s % 2) + i / 2);  // bit in little-endian word s / 2
+  const int b = 4 * i + 2 * (s % 2);  // bit in little-endian word s / 2: nibble i, low or high half
   *byte = static_cast<uint64_t>(tile) * 512 + lane * 8 + (s / 2) * 4 + b / 8;
   *bit = b % 8;
 }
@@ -150,15 +150,28 @@ inline uint64_t tiled_sb2_index(int K, int G, int n, int gi) {
 void permute_projection2(const uint8_t* src, uint8_t* dst, int N, int K, int G, int dir) {
   const uint64_t code_bytes = static_cast<uint64_t>(N) * K / 4;
   memset(dst, 0, code_bytes);
+  // (byte, bit) of column kk of a 128-k tile, relative to the tile and row
+  // (lane r = n % 16 of lane group 0): one table for every row and tile
+  uint16_t off[128];
+  uint8_t bitpos[128];
+  for (int kk = 0; kk < 128; ++kk) {
+    uint64_t b;
+    int bit;
+    tiled_code2_pos(128, 0, kk, &b, &bit);
+    off[kk] = static_cast<uint16_t>(b);
+    bitpos[kk] = static_cast<uint8_t>(bit);
+  }
   for (int n = 0; n < N; ++n) {
-    for (int k = 0; k < K; ++k) {
-      uint64_t tb;
-      int bit;
-      tiled_code2_pos(K, n, k, &tb, &bit);
-      const uint64_t cb = static_cast<uint64_t>(n) * (K / 4) + k / 4;
-      const int cbit = 2 * (k % 4);
-      if (dir > 0) dst[tb] |= static_cast<uint8_t>(((src[cb] >> cbit) & 3) << bit);
-      else dst[cb] |= static_cast<uint8_t>(((src[tb] >> bit) & 3) << cbit);
+    const uint8_t* crow = (dir > 0 ? src : dst) + static_cast<uint64_t>(n) * (K / 4);
+    for (int kt = 0; kt < K / 128; ++kt) {
+      const uint64_t tbase = (static_cast<uint64_t>(n / 16) * (K / 128) + kt) * 512 + (n % 16) * 8;
+      for (int kk = 0; kk < 128; ++kk) {
+        const int k = kt * 128 + kk;
+        const int cbit = 2 * (k % 4);
+        const uint64_t tb = tbase + off[kk];
+        if (dir > 0) dst[tb] |= static_cast<uint8_t>(((crow[k / 4] >> cbit) & 3) << bitpos[kk]);
+        else dst[static_cast<uint64_t>(n) * (K / 4) + k / 4] |= static_cast<uint8_t>(((src[tb] >> bitpos[kk]) & 3) << cbit);
+      }
     }
   }
   const uint64_t ng = static_cast<uint64_t>(N) * (K / G);  // groups; canonical scales then biases, 2 bytes each

@@ -122,13 +122,13 @@ def test_pack_mxfp8_matches_documented_layout_and_round_trips(shape):
 def _spec_affine2_code(packed, base, N, K, n, k):
     """Canonical 2-bit code (n, k) read from the device layout as include/moe.h
     describes it (512-byte tiles; lane 16g + r; word s // 2; the code of (s, i)
-    at bit 16 (i % 2) + 2 (4 (s % 2) + i // 2))."""
+    at bit 4 i + 2 (s % 2))."""
     tile = (n // 16) * (K // 128) + k // 128
     kk = k % 128
     s_, g, i = kk // 32, (kk % 32) // 8, kk % 8
     word = base + tile * 512 + (16 * g + n % 16) * 8 + 4 * (s_ // 2)
     w = int.from_bytes(bytes(packed[word:word + 4]), "little")
-    return (w >> (16 * (i % 2) + 2 * (4 * (s_ % 2) + i // 2))) & 3
+    return (w >> (4 * i + 2 * (s_ % 2))) & 3
 
 
 @pytest.mark.parametrize("shape", [(512, 512), (1024, 512), (512, 2048)])

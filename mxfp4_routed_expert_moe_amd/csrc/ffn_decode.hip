@@ -280,8 +280,9 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
   for (int i = 0; i < KTW; ++i) {
     if (i + RB - 1 < KTW) load_b((i + RB - 1) % RB, i + RB - 1);
     __builtin_amdgcn_sched_barrier(0);
-    // group by group: its row sums S, then per n-tile the group's MFMAs into
-    // a fresh P and the fold, so one P is live at a time
+    // group by group: its row sums S, then four n-tiles at a time the group's
+    // MFMAs into fresh P (four independent chains, so one n-tile's fold waits
+    // on no MFMA still in flight for it), then the folds
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
@@ -289,20 +290,27 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
       for (int ss = 0; ss < SPG; ++ss)
         S = mfma16x16x32(__builtin_bit_cast(bf16x8, a[i & 1][gi * SPG + ss]), ones, S);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < NT; j0 += 4) {
+        f32x4 P[4];
 #pragma unroll
-        for (int ss = 0; ss < SPG; ++ss) {
-          const int s = gi * SPG + ss;
-          const uint32_t w = bq[i % RB][j][s >> 1];
-          const bf16x8 bv = (s & 1) ? affine2_operand<1>(w) : affine2_operand<0>(w);
-          P = mfma16x16x32(__builtin_bit_cast(bf16x8, a[i & 1][s]), bv, P);
+        for (int jj = 0; jj < 4; ++jj) {
+          P[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ss = 0; ss < SPG; ++ss) {
+            const int s = gi * SPG + ss;
+            const uint32_t w = bq[i % RB][j0 + jj][s >> 1];
+            const bf16x8 bv = (s & 1) ? affine2_operand<1>(w) : affine2_operand<0>(w);
+            P[jj] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[i & 1][s]), bv, P[jj]);
+          }
         }
-        const uint32_t sbw = sq[i & 1][j][gi];
-        const float sc = __uint_as_float(sbw << 16);          // bf16 scale (low half)
-        const float bc = __uint_as_float(sbw & 0xffff0000u);  // bf16 bias (high half)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(bc, S[e], fmaf(sc, P[e], acc[j][e]));
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t sbw = sq[i & 1][j0 + jj][gi];
+          const float sc = __uint_as_float(sbw << 16);          // bf16 scale (low half)
+          const float bc = __uint_as_float(sbw & 0xffff0000u);  // bf16 bias (high half)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[j0 + jj][e] = fmaf(bc, S[e], fmaf(sc, P[jj][e], acc[j0 + jj][e]));
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);

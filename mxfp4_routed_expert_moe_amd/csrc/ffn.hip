@@ -11,10 +11,10 @@
 // of one MFMA B fragment.  Nothing is ever dequantised to memory.
 //
 // Two kernel families (ffn_decode.hip, ffn_prefill.hip):
-//  * decode (few rows per expert, HBM bound): a block takes one routed expert
-//    straight from the dispatch offsets, or one 16-row chunk of the shared
-//    group; its four waves split the K axis and the partial sums meet in LDS
-//    in a fixed order;
+//  * decode (few rows per expert, HBM bound; every T for 2-bit affine routed
+//    experts): a block takes one routed expert straight from the dispatch
+//    offsets, or one 16-row chunk of the shared group; its four waves split
+//    the K axis and the partial sums meet in LDS in a fixed order;
 //  * prefill (many rows per expert, MFMA bound): a device-side work list of
 //    items (group, first row, row count) of at most 64 rows, built here from
 //    the offsets so the host never learns the per-expert counts; the grid

@@ -5,8 +5,9 @@
 // ("Model techniques map -- DeepSeek-V4-Flash", row "SwiGLU feed-forward";
 // MXFP4 weights as in "ElytronAI / DeepSeek-v4-Flash", Sizes), streaming the
 // expert's tiled MXFP4 bytes (or an MXFP8 shared expert's, the same page's
-// dense format) once from HBM into bf16 MFMA B fragments via the hardware
-// scaled FP4 / FP8 converts.
+// dense format, or 2-bit affine routed experts' codes, "OsaurusAI /
+// DeepSeek-V4-Flash-0731-JANG", Dynamic affine recipe) once from HBM into
+// bf16 MFMA B fragments via the hardware scaled FP4 / FP8 converts.
 #include "ffn_internal.h"
 
 namespace moe {
@@ -191,10 +192,10 @@ __device__ __forceinline__ bf16x8 affine2_operand(uint32_t w) {
 // the row sums of x over the group), and each group is folded into the
 // float32 accumulator with two multiply-adds per element.  (The bias term as
 // MFMAs of x against the broadcast bias, instead of S and a multiply-add,
-// measured slower: the matrix cores are as busy as the vector unit here.)  MFMA s of a 128-k
-// tile covers k = 32 s .. 32 s + 31 (lane 16 g + r: k = 32 s + 8 g + 0..7), so
-// an MFMA never straddles two groups.  Same block shape, split-K and
-// epilogue as the MX chunk.
+// measured slower: the matrix cores are as busy as the vector unit here.)
+// MFMA s of a 128-k tile covers k = 32 s .. 32 s + 31 (lane 16 g + r: k =
+// 32 s + 8 g + 0..7), so an MFMA never straddles two groups.  Same block
+// shape, split-K and epilogue as the MX chunk.
 template <bool GATEUP, int KTW>
 __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act,
                                                 const int32_t* __restrict__ row_token, int g, int row0, int nrows,

@@ -211,7 +211,7 @@ def main():
     shared_proj = H * I * 33 // 32 if args.shared_mxfp8 else mx4_proj
     gateup_bytes = (used - 1) * 2 * gate_proj + 2 * shared_proj + rows * H * 2 + rows * I * 2
     gateup_flops = rows * 2 * 2 * H * I
-    decode = rows <= 16 * (E + 1) or args.routed_affine2   # the affine codec runs the decode family at every T
+    decode = rows <= 16 * (E + 1)
     if decode:
         achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -11,10 +11,10 @@
 // of one MFMA B fragment.  Nothing is ever dequantised to memory.
 //
 // Two kernel families (ffn_decode.hip, ffn_prefill.hip):
-//  * decode (few rows per expert, HBM bound; every T for 2-bit affine routed
-//    experts): a block takes one routed expert straight from the dispatch
-//    offsets, or one 16-row chunk of the shared group; its four waves split
-//    the K axis and the partial sums meet in LDS in a fixed order;
+//  * decode (few rows per expert, HBM bound): a block takes one routed expert
+//    straight from the dispatch offsets, or one 16-row chunk of the shared
+//    group; its four waves split the K axis and the partial sums meet in LDS
+//    in a fixed order;
 //  * prefill (many rows per expert, MFMA bound): a device-side work list of
 //    items (group, first row, row count) of at most 64 rows, built here from
 //    the offsets so the host never learns the per-expert counts; the grid
@@ -90,23 +90,21 @@ __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict
 }
 
 // Decode kernels while the average group holds at most ~16 rows (and both K
-// sizes have a compiled decode variant), and for 2-bit affine routed experts
-// at every T (the validation has checked both K sizes); prefill kernels
-// otherwise.
-inline bool use_decode(int T, int E, int k, int H, int I, bool routed_a2) {
-  return routed_a2 || (static_cast<long>(T) * (k + 1) <= 16L * (E + 1) && decode_k_ok(H) && decode_k_ok(I));
+// sizes have a compiled decode variant, which the validation requires for
+// 2-bit affine routed experts); prefill kernels otherwise.
+inline bool use_decode(int T, int E, int k, int H, int I) {
+  return static_cast<long>(T) * (k + 1) <= 16L * (E + 1) && decode_k_ok(H) && decode_k_ok(I);
 }
 
-inline int ffn_bm(int T, int E, int k, int H, int I, bool routed_a2) {
-  return use_decode(T, E, k, H, I, routed_a2) ? kDecodeRows : kPrefillRows;
-}
+inline int ffn_bm(int T, int E, int k, int H, int I) { return use_decode(T, E, k, H, I) ? kDecodeRows : kPrefillRows; }
 
 }  // namespace
 
 size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool routed_a2) {
-  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I, routed_a2));
+  (void)routed_a2;  // same workspace as MXFP4 routed experts
+  const int mi = ffn_max_items(T, E, k, ffn_bm(T, E, k, H, I));
   const size_t n = 256 + align256(sizeof(int4) * static_cast<size_t>(mi));
-  if (split_fp8 && !use_decode(T, E, k, H, I, routed_a2))
+  if (split_fp8 && !use_decode(T, E, k, H, I))
     return n + qact_bytes(T, H) + qact_bytes(static_cast<long>(T) * (k + 1), I);
   return n + align256(sizeof(uint16_t) * static_cast<size_t>(T) * (k + 1) * I);
 }
@@ -114,9 +112,9 @@ size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool rout
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
                       void* ws, int phase, bool split_fp8, bool shared_w8, bool routed_a2, hipStream_t s) {
-  const int bm = ffn_bm(T, E, k, H, I, routed_a2);
+  const int bm = ffn_bm(T, E, k, H, I);
   const int max_items = ffn_max_items(T, E, k, bm);
-  const bool dec = use_decode(T, E, k, H, I, routed_a2);
+  const bool dec = use_decode(T, E, k, H, I);
   const bool split = split_fp8 && !dec;
   FfnWs w = ffn_carve(ws, max_items, T, k, H, I, split);
   for (int ph = 0; ph < 3; ++ph) {
@@ -138,7 +136,7 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
                               max_items, s);
       } else {
         launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, T, E, shared_w8,
-                           s);
+                           routed_a2, s);
       }
     }
   }

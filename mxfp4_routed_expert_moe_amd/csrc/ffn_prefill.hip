@@ -43,44 +43,67 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 // That covers every logical block only if the grid has at least
 // 8 * ceil(total / 8) blocks: launches add kGridSlack rows of blocks.
 //
-// W8: the items of an MXFP8 shared expert (group skip_g of the MXFP4 launch),
-// which are the last n_w8 items of the work list.  Its 2048-byte weight
-// tiles are read as two 1 KiB halves into a two-stage register ring (the
-// same registers as four MXFP4 stages), one tile ahead: each tile drains the
-// wave's loads and passes the barrier, then issues the next tile.
-template <bool GATEUP, bool W8>
+// A launch covers the whole work list, or (n_tail > 0) only its last n_tail
+// items -- the shared expert's, which come last -- and its blocks of group
+// skip_g return at once (that group runs in a launch of its own).
+//
+// FMT kFmtMx8: an MXFP8 shared expert.  Its 2048-byte weight tiles are read
+// as two 1 KiB halves into a two-stage register ring (the same registers as
+// four MXFP4 stages), one tile ahead: each tile drains the wave's loads and
+// passes the barrier, then issues the next tile.
+//
+// FMT kFmtA2: 2-bit affine routed experts ("OsaurusAI /
+// DeepSeek-V4-Flash-0731-JANG", Dynamic affine recipe).  Each 512-byte code
+// tile (8 bytes a lane) and its (scale, bias) words ride in the MXFP4 ring
+// and pipeline; per group of G input columns (64 for gate and up, 32 for
+// down) the MFMAs run x against the exact bf16 codes q (P) and against ones
+// (S, the row sums of x over the group), and acc += s * P + b * S -- the
+// group's sum x . (s q + b), regrouped.
+constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;
+
+template <bool GATEUP, int FMT>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
                                                              const int32_t* __restrict__ n_items,
                                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes,
-                                                             int H, int I, float limit, int skip_g, int n_w8,
+                                                             int H, int I, float limit, int skip_g, int n_tail,
                                                              uint16_t* __restrict__ h_out,
                                                              float* __restrict__ out_rows) {
+  constexpr bool W8 = FMT == kFmtMx8;
+  constexpr bool A2 = FMT == kFmtA2;
   constexpr int kNT = kNT4;           // weight n-tiles per wave
   constexpr int NQ = W8 ? 2 : 1;      // 16-byte loads per lane per n-tile per k tile
-  constexpr uint64_t kTileBytes = W8 ? 2048 : 1024;
+  constexpr uint64_t kTileBytes = W8 ? 2048 : A2 ? 512 : 1024;
+  constexpr int G = GATEUP ? 64 : 32;  // affine group size
+  constexpr int NG = 128 / G;          // affine groups per k tile
+  constexpr int SPG = G / 32;          // MFMA k steps per affine group
+  constexpr uint64_t kSbBytes = 16 * NG * 4;  // affine (scale, bias) words of a 16 x 128 tile
+  typedef __attribute__((__vector_size__(NG * sizeof(unsigned)))) unsigned u32xg;
   __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
   const int nbc = gridDim.x;
-  const int total = (W8 ? n_w8 : *n_items) * nbc;
+  const int nit = *n_items;
+  const int total = (n_tail > 0 ? n_tail : nit) * nbc;
   const int b = blockIdx.x + blockIdx.y * nbc;
   const int per = (total + 7) >> 3;
   if ((b >> 3) >= per) return;
   const int lam = (b & 7) * per + (b >> 3);
   if (lam >= total) return;
-  const int4 it = items[(W8 ? *n_items - n_w8 : 0) + lam / nbc];
+  const int4 it = items[(n_tail > 0 ? nit - n_tail : 0) + lam / nbc];
   const int nb = lam % nbc;
   const int g = it.x, row0 = it.y, nrows = it.z;
-  if (!W8 && g == skip_g) return;  // the MXFP8 shared expert's items run in their own launch
+  if (g == skip_g) return;  // this group's items run in a launch of their own
   const int K = GATEUP ? H : I;
   const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const ExpertPlanes pl = W8 ? expert_planes8(H, I) : expert_planes(H, I);
+  const ExpertPlanes pl = W8 ? expert_planes8(H, I) : A2 ? expert_planes_a2(H, I) : expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
   const uint64_t tstride = static_cast<uint64_t>(KT) * kTileBytes;  // bytes between n-tiles
-  const uint64_t sstride = static_cast<uint64_t>(KT >> 2) * 256;
+  // bytes between n-tiles of the scale plane (MX: one 256-byte block per 4 k
+  // tiles; affine: kSbBytes per k tile)
+  const uint64_t sstride = A2 ? static_cast<uint64_t>(KT) * kSbBytes : static_cast<uint64_t>(KT >> 2) * 256;
 
   const uint8_t* nb0;
   const uint8_t* nb1;
@@ -99,10 +122,11 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
     sb0 = eb + pl.down_sc + nt0 * sstride;
     sb1 = sb0 + (kNT / 2) * sstride;
   }
-  nb0 += lane * 16;
-  nb1 += lane * 16;
-  sb0 += lane * 4;
-  sb1 += lane * 4;
+  nb0 += lane * (A2 ? 8 : 16);
+  nb1 += lane * (A2 ? 8 : 16);
+  // affine: the (scale, bias) words of output column lane % 16 (MFMA result layout)
+  sb0 += A2 ? (lane & 15) * (NG * 4) : lane * 4;
+  sb1 += A2 ? (lane & 15) * (NG * 4) : lane * 4;
 
   // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
@@ -116,14 +140,24 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   }
 
   constexpr int kH = kNT / 2;
-  u32x4 bq[W8 ? 2 : kStages][kNT][NQ];  // W8: a two-stage ring (twice the bytes per tile)
+  u32x4 bq[A2 ? 1 : W8 ? 2 : kStages][kNT][NQ];  // W8: a two-stage ring (twice the bytes per tile)
+  u32x2 bq2[A2 ? kStages : 1][kNT];              // affine codes
+  u32xg sq2[A2 ? kStages : 1][kNT];              // affine (scale, bias) words
   uint32_t sw[kNT], swn[kNT];
   auto issue_tile = [&](int stage, int kt) {
+    if constexpr (A2) {
 #pragma unroll
-    for (int j = 0; j < kNT; ++j)
+      for (int j = 0; j < kNT; ++j) {
+        bq2[stage][j] = *reinterpret_cast<const u32x2*>((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes);
+        sq2[stage][j] = *reinterpret_cast<const u32xg*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + kt * kSbBytes);
+      }
+    } else {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        bq[stage][j][q] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes + q * 1024);
+      for (int j = 0; j < kNT; ++j)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          bq[stage][j][q] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes + q * 1024);
+    }
 #pragma unroll
     for (int q = 0; q < kDmaOps; ++q)
       __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
@@ -172,6 +206,56 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
       }
     }
   };
+  // Affine tile kt from LDS stage st (codes and (scale, bias) words in ring
+  // stage st): group by group, the row sums S of each row tile, then per
+  // n-tile the group's MFMAs into fresh P (four row-tile chains) and the folds.
+  auto compute_tile_a2 = [&](int st) {
+    const uint16_t* abuf = As[st];
+    const u32x4 ones_w = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      bf16x8 a[SPG][4];
+      f32x4 S[4];
+#pragma unroll
+      for (int ss = 0; ss < SPG; ++ss) {
+        const int s = gi * SPG + ss;
+        // MFMA step s takes k = 32 s + 8 (lane / 16) + 0..7: 16-byte chunk 4 s + lane / 16 of the row
+        const int slot = ((4 * s + g4) ^ (lane & 15)) * 8;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) a[ss][mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ss = 0; ss < SPG; ++ss) S[mt] = mfma16x16x32(a[ss][mt], ones, S[mt]);
+      }
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        f32x4 P[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ss = 0; ss < SPG; ++ss) {
+          const int s = gi * SPG + ss;
+          // code i of step s: bits 4i + 2 (s % 2) of word s / 2 -> E2M1 nibbles 00qq = q / 2
+          const uint32_t w = bq2[st][j][s >> 1];
+          const uint32_t nib = ((s & 1) ? (w >> 2) : w) & 0x33333333u;
+          const bf16x8 bv = dequant8(nib, e8m0_scale_operand(128u));  // scale 2: the bf16 values q
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) P[mt] = mfma16x16x32(a[ss][mt], bv, P[mt]);
+        }
+        const uint32_t sbw = sq2[st][j][gi];
+        const float sc = __uint_as_float(sbw << 16);          // bf16 scale (low half)
+        const float bc = __uint_as_float(sbw & 0xffff0000u);  // bf16 bias (high half)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mt][j][e] = fmaf(bc, S[mt][e], fmaf(sc, P[mt][e], acc[mt][j][e]));
+      }
+    }
+  };
   if constexpr (W8) {
     issue_scales(sw, 0);
     issue_tile(0, 0);
@@ -195,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
       }
     }
   } else {
-    issue_scales(sw, 0);
+    if (!A2) issue_scales(sw, 0);
     issue_tile(0, 0);
     issue_tile(1, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -212,14 +296,24 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
           wait_vmcnt<0>();
           lds_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          if (i == 0 && !last) issue_scales(swn, u + 1);
+          if (!A2 && i == 0 && !last) issue_scales(swn, u + 1);
           if (kt + 2 < KT) issue_tile((i + 2) % kStages, kt + 2);
           if (kt + 3 < KT) issue_tile((i + 3) % kStages, kt + 3);
           __builtin_amdgcn_sched_barrier(0);
         }
-        compute_tile(i, i, i);
+        if constexpr (A2) {
+          compute_tile_a2(i);
+          // keep each tile's MFMAs and folds above the next barrier (the
+          // compiler otherwise sinks them and runs out of registers)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j) asm volatile("" : "+v"(acc[mt][j]));
+        } else {
+          compute_tile(i, i, i);
+        }
       }
-      if (!last) {
+      if (!A2 && !last) {
 #pragma unroll
         for (int j = 0; j < kNT; ++j) sw[j] = swn[j];
       }
@@ -261,24 +355,39 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
-                        int T, int E, bool shared_w8, hipStream_t s) {
-  // the MXFP8 shared expert's items (the last ceil(T / 64) of the work list) in a launch of their own
-  const int skip = shared_w8 ? E : -1;
+                        int T, int E, bool shared_w8, bool routed_a2, hipStream_t s) {
+  // The routed experts' launch (MXFP4, with an MXFP4 shared expert riding
+  // along, or 2-bit affine), then the shared expert's own launch over the last
+  // ceil(T / 64) items of the work list when it has another format.
+  const bool own_shared = shared_w8 || routed_a2;
+  const int skip = own_shared ? E : -1;
   const int nsh = (T + kPrefillRows - 1) / kPrefillRows;
-  const int ny = max_items + kGridSlack, ny8 = nsh + kGridSlack;
+  const int ny = max_items + kGridSlack, ny_sh = nsh + kGridSlack;
+  const dim3 grid(gateup ? I / 128 : H / 256, ny), grid_sh(gateup ? I / 128 : H / 256, ny_sh);
+  uint16_t* ho = gateup ? w.h : nullptr;
+  float* oo = gateup ? nullptr : out_rows;
+  const int32_t* rt = gateup ? row_token : nullptr;
+#define MOE_PREFILL(G)                                                                                            \
+  do {                                                                                                          \
+    if (routed_a2)                                                                                              \
+      ffn_prefill_kernel<G, kFmtA2><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I, limit, \
+                                                              skip, 0, ho, oo);                                 \
+    else                                                                                                        \
+      ffn_prefill_kernel<G, kFmtMx4><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,      \
+                                                               limit, skip, 0, ho, oo);                         \
+    if (shared_w8)                                                                                              \
+      ffn_prefill_kernel<G, kFmtMx8><<<grid_sh, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,   \
+                                                                  limit, -1, nsh, ho, oo);                      \
+    else if (routed_a2)                                                                                         \
+      ffn_prefill_kernel<G, kFmtMx4><<<grid_sh, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,   \
+                                                                  limit, -1, nsh, ho, oo);                      \
+  } while (0)
   if (gateup) {
-    ffn_prefill_kernel<true, false><<<dim3(I / 128, ny), kThreads, 0, s>>>(
-        act, row_token, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, w.h, nullptr);
-    if (shared_w8)
-      ffn_prefill_kernel<true, true><<<dim3(I / 128, ny8), kThreads, 0, s>>>(act, row_token, w.items, w.n_items, blob,
-                                                                           eb, H, I, limit, -1, nsh, w.h, nullptr);
+    MOE_PREFILL(true);
   } else {
-    ffn_prefill_kernel<false, false><<<dim3(H / 256, ny), kThreads, 0, s>>>(
-        act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, skip, 0, nullptr, out_rows);
-    if (shared_w8)
-      ffn_prefill_kernel<false, true><<<dim3(H / 256, ny8), kThreads, 0, s>>>(
-          act, nullptr, w.items, w.n_items, blob, eb, H, I, limit, -1, nsh, nullptr, out_rows);
+    MOE_PREFILL(false);
   }
+#undef MOE_PREFILL
 }
 
 }  // namespace moe

@@ -206,7 +206,7 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* off
 
 // split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8);
 // shared_w8: the shared expert is MXFP8 (MOE_SHARED_MXFP8); routed_a2: the
-// routed experts are 2-bit affine (MOE_ROUTED_AFFINE2: decode family at every T).
+// routed experts are 2-bit affine (MOE_ROUTED_AFFINE2).
 size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool routed_a2);
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
                       int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,

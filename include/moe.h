@@ -85,9 +85,9 @@ extern "C" {
  * (= H * I: 2.5, 2.5 and 3 bits per weight).  The shared expert, slot
  * n_experts at base + n_experts * expert_bytes, keeps an MX layout: MXFP4
  * (moe_expert_bytes(H, I) bytes) or, with MOE_SHARED_MXFP8, MXFP8 -- the
- * recipe's shared expert is 8-bit.  The FFN runs its decode kernel family at
- * every token count, so H and I must each be 512, 1024, 2048 or 4096
- * (MOE_ESHAPE otherwise).  Not combinable with MOE_FFN_SPLIT_FP8 (MOE_EINVAL).
+ * recipe's shared expert is 8-bit.  H and I must each be 512, 1024, 2048 or
+ * 4096 (MOE_ESHAPE otherwise: the decode kernel family has no other sizes
+ * for this codec).  Not combinable with MOE_FFN_SPLIT_FP8 (MOE_EINVAL).
  * The 3-bit gate of six listed layers in the same recipe is not supported.
  */
 #define MOE_ROUTED_AFFINE2 4

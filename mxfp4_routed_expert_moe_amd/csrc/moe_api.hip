@@ -28,7 +28,7 @@ int check_experts(const moe_experts* d) {
   const bool a2 = (d->flags & MOE_ROUTED_AFFINE2) != 0;
   const uint64_t eb = a2 ? moe_expert_bytes_affine2(d->hidden, d->inter) : moe_expert_bytes(d->hidden, d->inter);
   if (eb == 0 || d->expert_bytes != eb) return MOE_ESHAPE;
-  // the affine codec runs the decode kernel family at every token count
+  // the affine codec's decode-family kernels exist for these K sizes only
   if (a2 && !(moe::decode_k_ok(d->hidden) && moe::decode_k_ok(d->inter))) return MOE_ESHAPE;
   if (!aligned(d->base, 256)) return MOE_EALIGN;
   return MOE_OK;

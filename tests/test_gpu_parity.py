@@ -480,8 +480,9 @@ def test_shared_mxfp8_full_workloads(index, sample):
     torch.cuda.empty_cache()
 
 
-# The routed experts in the 2-bit affine codec (MOE_ROUTED_AFFINE2): the
-# decode kernel family at every T, the shared expert in its own MX launch.
+# The routed experts in the 2-bit affine codec (MOE_ROUTED_AFFINE2): both
+# kernel families; an MXFP4 shared expert rides in the decode launch and has
+# its own prefill launch, an MXFP8 one has its own launches.
 def _affine2_inputs(T, H, I, E, seed, routing="learned", shared="mxfp4"):
     inp = _small_inputs(T, H, I, E, seed, routing)
     inp.experts = WL.make_experts_affine2(seed, E, H, I, shared)
@@ -492,8 +493,9 @@ def _affine2_inputs(T, H, I, E, seed, routing="learned", shared="mxfp4"):
     (5, 512, 1024, 16, "learned", "mxfp4"),     # one chunk per group
     (37, 512, 512, 16, "learned", "mxfp4"),     # routed groups and the shared group over 16 rows: several chunks
     (61, 1024, 512, 64, "hash", "mxfp4"),       # hash routing; gate/up K = 1024
-    (300, 512, 512, 16, "learned", "mxfp4"),    # a prefill-sized T on the decode family (~112 rows per expert)
-    (200, 1024, 2048, 32, "learned", "mxfp4"),  # down K = 2048 (four k tiles per wave, two-deep code ring)
+    (300, 512, 512, 16, "learned", "mxfp4"),    # prefill family, ragged 64-row items (~112 rows per expert)
+    (200, 1024, 2048, 32, "learned", "mxfp4"),  # prefill family, gate/up K = 1024 (groups of 64), down K = 2048 (32)
+    (40, 512, 2048, 64, "learned", "mxfp4"),    # decode family, down K = 2048 (four k tiles per wave, two-deep ring)
     (37, 512, 512, 16, "learned", "mxfp8"),     # with the MXFP8 shared expert (the recipe's 8-bit shared expert)
     (9, 4096, 512, 16, "learned", "mxfp8"),     # gate/up K = 4096 (eight k tiles per wave)
 ])

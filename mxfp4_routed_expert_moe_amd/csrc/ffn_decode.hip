@@ -359,8 +359,6 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
   }
 }
 
-constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;  // weight format of the groups a launch covers
-
 // grid (n blocks, nrouted + ceil(T / 16)), 64 * kWaves threads: block row y <
 // nrouted takes the rows of routed expert y (16 at a time; an expert with no
 // rows returns at once), the rest take 16-row chunks of the shared group, so

@@ -24,6 +24,10 @@ struct FfnWs {
   QAct hq;           // [rows, I] (prefill)
 };
 
+// Weight format of the groups a kernel instance covers: MXFP4, MXFP8 (the
+// shared expert, MOE_SHARED_MXFP8), 2-bit affine (routed, MOE_ROUTED_AFFINE2).
+constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;
+
 constexpr int kDecodeRows = 16;    // rows per decode item
 constexpr int kPrefillRows = 64;   // rows per prefill item
 // Extra rows of blocks in the prefill grids: their XCD-aware block order

@@ -59,8 +59,6 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 // down) the MFMAs run x against the exact bf16 codes q (P) and against ones
 // (S, the row sums of x over the group), and acc += s * P + b * S -- the
 // group's sum x . (s q + b), regrouped.
-constexpr int kFmtMx4 = 0, kFmtMx8 = 1, kFmtA2 = 2;
-
 template <bool GATEUP, int FMT>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,

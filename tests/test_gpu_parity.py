@@ -39,14 +39,16 @@ def _experts(inp):
 # T*7 <= 16*(E+1) selects the decode kernels, above it the prefill kernels.
 SMALL = [
     # (T, H, I, E, routing, bias)
-    (1, 512, 512, 16, "learned", False),      # decode, one m-tile, 1 row per expert
-    (5, 512, 1024, 16, "learned", False),     # decode, MT=1
-    (29, 1024, 512, 32, "learned", True),     # decode, MT=2, selection bias
-    (37, 512, 512, 16, "learned", False),     # decode, MT=4 (shared group spans 3 m-tiles)
+    (1, 512, 512, 16, "learned", False),      # decode, 1 row per expert
+    (5, 512, 1024, 16, "learned", False),     # decode, every group in one 16-row chunk
+    (29, 1024, 512, 32, "learned", True),     # decode, selection bias
+    (37, 512, 512, 16, "learned", False),     # decode, groups over 16 rows (the shared one: 3 chunks)
     (61, 512, 512, 16, "hash", False),        # hash routing
     (300, 512, 512, 16, "learned", False),    # prefill, ragged 64-row items
     (700, 512, 512, 256, "learned", False),   # prefill, 256 experts, many tiny groups
     (64, 512, 512, 256, "learned", True),     # decode with 256 experts, many empty
+    (9, 512, 4096, 16, "learned", False),     # decode, down K = 4096 (eight k tiles per wave)
+    (200, 2048, 4096, 16, "learned", False),  # prefill, K = 2048 and 4096
 ]
 
 
@@ -498,6 +500,8 @@ def _affine2_inputs(T, H, I, E, seed, routing="learned", shared="mxfp4"):
     (40, 512, 2048, 64, "learned", "mxfp4"),    # decode family, down K = 2048 (four k tiles per wave, two-deep ring)
     (37, 512, 512, 16, "learned", "mxfp8"),     # with the MXFP8 shared expert (the recipe's 8-bit shared expert)
     (9, 4096, 512, 16, "learned", "mxfp8"),     # gate/up K = 4096 (eight k tiles per wave)
+    (9, 512, 4096, 16, "learned", "mxfp4"),     # down K = 4096 (eight k tiles per wave)
+    (200, 2048, 4096, 16, "learned", "mxfp4"),  # prefill family, K = 2048 and 4096
 ])
 def test_affine2_small_shapes(T, H, I, E, routing, shared):
     print(f"[parity] affine2 T={T} H={H} I={I} E={E} {routing} shared {shared}", flush=True)

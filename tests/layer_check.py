@@ -46,13 +46,17 @@ def run_gpu_layer(inp: WL.LayerInputs, experts: B.Experts, T: int | None = None,
                 y=host(layer.y).view(np.uint16), layer=layer)
 
 
-def oracle_routing(inp: WL.LayerInputs):
+def oracle_routing(inp: WL.LayerInputs, toks=None):
+    """Oracle ids, weights and selection gaps of every token, or of the tokens
+    toks (routing is per token, so a subset is computed on its own)."""
+    x = inp.x if toks is None else inp.x[toks]
     if inp.table is not None:
-        ids, w = O.route_hash(inp.tok, inp.table, inp.top_k, WL.ROUTE_SCALE)
+        tok = inp.tok if toks is None else inp.tok[toks]
+        ids, w = O.route_hash(tok, inp.table, inp.top_k, WL.ROUTE_SCALE)
         gap = np.full(len(ids), np.inf)
     else:
-        ids, w, _ = O.route_learned(inp.x, inp.router, inp.bias, inp.top_k, WL.ROUTE_SCALE)
-        gap = O.boundary_gap(inp.x, inp.router, inp.bias, inp.top_k)
+        ids, w, _ = O.route_learned(x, inp.router, inp.bias, inp.top_k, WL.ROUTE_SCALE)
+        gap = O.boundary_gap(x, inp.router, inp.bias, inp.top_k)
     return ids, w, gap
 
 
@@ -70,13 +74,16 @@ def assert_output_close(got, ref, what=""):
     return mx, mean
 
 
-def check_routing(g, ids_ref, w_ref, gap):
-    """Bit-exact ids (tokens on a near tie, if any, are reported and skipped)."""
+def check_routing(g, ids_ref, w_ref, gap, toks=None):
+    """Bit-exact ids (tokens on a near tie, if any, are reported and skipped);
+    ids_ref, w_ref and gap cover every token, or the tokens toks."""
+    ids = g["ids"] if toks is None else g["ids"][toks]
+    wts = g["weights"] if toks is None else g["weights"][toks]
     clear = gap >= AMBIGUOUS_GAP
     assert clear.mean() > 0.99
-    assert np.array_equal(g["ids"][clear], ids_ref[clear])
+    assert np.array_equal(ids[clear], ids_ref[clear])
     wr = w_ref[clear]
-    assert np.max(np.abs(g["weights"][clear] - wr) / np.abs(wr)) <= W_REL
+    assert np.max(np.abs(wts[clear] - wr) / np.abs(wr)) <= W_REL
     return int((~clear).sum())
 
 
@@ -90,46 +97,53 @@ def check_dispatch(g, ids_gpu, E):
 
 
 def full_check(inp: WL.LayerInputs, experts: B.Experts, sample_tokens=None, seed=0, shared_fmt="mxfp4",
-               routed_fmt="mxfp4"):
+               routed_fmt="mxfp4", route_sample=None):
     """Whole-layer parity: routing, dispatch, expert rows and y.  With
     sample_tokens, the expert rows and outputs are checked on that many
-    randomly chosen tokens (the oracle computes each one on its own).
-    shared_fmt, routed_fmt: the weight formats of the shared and the routed
-    experts in inp.experts."""
+    randomly chosen tokens (the oracle computes each one on its own).  With
+    route_sample, the routing is checked on that many random tokens plus the
+    first and the last (dispatch is still checked on every pair, from the
+    GPU's ids).  shared_fmt, routed_fmt: the weight formats of the shared and
+    the routed experts in inp.experts."""
     g = run_gpu_layer(inp, experts)
-    ids_ref, w_ref, gap = oracle_routing(inp)
-    n_amb = check_routing(g, ids_ref, w_ref, gap)
-    off, rt, sr = check_dispatch(g, g["ids"], inp.n_experts)
     T = inp.x.shape[0]
-    if sample_tokens is None or sample_tokens >= T:
-        toks = np.arange(T)
+    if route_sample is None or route_sample >= T:
+        rtoks = np.arange(T)
     else:
-        toks = np.sort(np.random.default_rng(seed).choice(T, sample_tokens, replace=False))
-    toks = toks[gap[toks] >= AMBIGUOUS_GAP]      # a token on a near tie has two correct answers
+        pick = np.random.default_rng([seed, 1]).choice(T, route_sample, replace=False)
+        rtoks = np.unique(np.concatenate([pick, [0, T - 1]]))
+    ids_ref, w_ref, gap = oracle_routing(inp, None if len(rtoks) == T else rtoks)
+    n_amb = check_routing(g, ids_ref, w_ref, gap, None if len(rtoks) == T else rtoks)
+    off, rt, sr = check_dispatch(g, g["ids"], inp.n_experts)
+    # rows and y on a sample of the routing-checked tokens (positions in rtoks)
+    if sample_tokens is None or sample_tokens >= len(rtoks):
+        pos = np.arange(len(rtoks))
+    else:
+        pos = np.sort(np.random.default_rng(seed).choice(len(rtoks), sample_tokens, replace=False))
+    pos = pos[gap[pos] >= AMBIGUOUS_GAP]      # a token on a near tie has two correct answers
+    toks = rtoks[pos]
     rows = sr[toks].reshape(-1)
     rows = rows[rows >= 0]
     # oracle expert rows for the sampled rows only, expert-major
-    x = inp.x
-    xf = O.bf16_bits_to_f64(x)
     ref_rows = {}
     grp = np.searchsorted(off, rows, side="right") - 1
     for e in np.unique(grp):
         fmt = shared_fmt if int(e) == inp.n_experts else routed_fmt
         mats = O.decode_expert(inp.experts, int(e), inp.hidden, inp.inter, fmt, routed_fmt)
         rs = rows[grp == e]
-        o = O.expert_forward(xf[rt[rs]], mats, WL.CLAMP_LIMIT)
+        o = O.expert_forward(O.bf16_bits_to_f64(inp.x[rt[rs]]), mats, WL.CLAMP_LIMIT)
         for r, v in zip(rs, o):
             ref_rows[int(r)] = v
-    got_rows = host(g["out_rows"][np.asarray(sorted(ref_rows), dtype=np.int64)])
-    want_rows = np.stack([ref_rows[r] for r in sorted(ref_rows)])
+    kept = np.asarray(sorted(ref_rows), dtype=np.int64)
+    got_rows = host(g["out_rows"][kept])
+    want_rows = np.stack([ref_rows[int(r)] for r in kept])
     rows_err = assert_output_close(got_rows, want_rows, "expert rows")
     # y of the sampled tokens from the oracle's rows and the oracle's weights
-    # (routing matched, so the GPU's ids index the same rows)
-    out_s = np.zeros((int(off[-1]), inp.hidden))
-    for r, v in ref_rows.items():
-        out_s[r] = v
-    w_use = w_ref.copy()
-    y_ref = O.combine(out_s, sr[toks], w_use[toks])
+    # (routing matched, so the GPU's ids index the same rows); the rows are
+    # held compactly, slot_row renumbered to match (dropped slots stay -1)
+    sr_s = sr[toks].astype(np.int64)
+    sr_c = np.where(sr_s >= 0, np.searchsorted(kept, sr_s), -1)
+    y_ref = O.combine(want_rows, sr_c, w_ref[pos])
     y_got = O.bf16_bits_to_f64(g["y"][toks])
     y_err = assert_output_close(y_got, y_ref, "layer output")
     return dict(g=g, rows_err=rows_err, y_err=y_err, ambiguous=n_amb, tokens=toks)

@@ -368,6 +368,30 @@ def test_full_workloads(index, sample):
     torch.cuda.empty_cache()
 
 
+# The largest batch the boundary accepts: MOE_MAX_TOKENS tokens on the
+# Zipf-skewed router of the 16384-token workload (the hottest expert takes
+# nearly every token, 4096 items of 64 rows).  7 * 262144 rows of H = 4096
+# put most element offsets into out_rows, h and the activations past 2^31.
+# Routing is checked on 1024 random tokens plus the first and the last,
+# dispatch on every pair, expert rows and outputs on 4 tokens.
+def test_max_tokens():
+    w = WL.WORKLOADS[4]
+    T = B.MOE_MAX_TOKENS
+    print(f"[parity] {w.name} router at T={T}", flush=True)
+    _, ex = _full_inputs(4)
+    inp = WL.make_layer_inputs(w, T=T, experts=_EXPERTS_CACHE[w.seed][0])
+    r = LC.full_check(inp, ex, sample_tokens=4, seed=7, route_sample=1024)
+    off = r["g"]["offsets"]
+    assert int(off[-1]) > (1 << 31) // WL.HIDDEN             # rows whose element offsets pass 2^31
+    assert np.diff(off[: WL.N_EXPERTS + 1]).max() >= 0.98 * T
+    sr = r["g"]["slot_row"][r["tokens"]]
+    assert len(r["tokens"]) > 0 and (int(sr.max()) + 1) * WL.HIDDEN > 1 << 31   # checked rows past 2^31
+    print(f"[parity] T={T}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
+    del r, inp
+    torch.cuda.empty_cache()
+
+
 # The prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8).
 @pytest.mark.parametrize("T,H,I,E", [(300, 512, 512, 16), (700, 512, 512, 256), (200, 1024, 2048, 32)])
 def test_split_fp8_small_shapes(T, H, I, E):

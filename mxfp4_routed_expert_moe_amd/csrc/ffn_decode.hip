@@ -31,10 +31,17 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
   constexpr int NH = NT / 2;
   constexpr int NQ = W8 ? 2 : 1;      // 16-byte loads per lane per n-tile per k tile
   constexpr uint64_t kTileBytes = W8 ? 2048 : 1024;
-  constexpr int NSW = KTW >= 4 ? KTW / 4 : 1;  // scale words per n-tile per wave
+  // The down projection's waves interleave over the k tiles (wave w takes
+  // tiles w, w + 4, ...: scale group i, byte w), so at each step a block reads
+  // four consecutive tiles of every n-tile; this measured faster than
+  // contiguous quarters.  The gate/up waves (8 tiles each, which would need 8
+  // scale words per n-tile) and K = 4096 keep contiguous quarters.
+  constexpr bool IL = !GATEUP && KTW <= 4;
+  constexpr int KS = IL ? kWaves : 1;                       // k-tile step of a wave
+  constexpr int NSW = IL ? KTW : (KTW >= 4 ? KTW / 4 : 1);  // scale words per n-tile per wave
   static_assert(KTW % 4 == 0 || 4 % KTW == 0, "a wave's k tiles tile its scale words");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kt0 = wave * KTW;
+  const int kt0 = IL ? wave : wave * KTW;
   const ExpertPlanes pl = W8 ? expert_planes8(H, I) : expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
   constexpr uint64_t kTileStride = static_cast<uint64_t>(KT) * kTileBytes;  // bytes between n-tiles
@@ -81,11 +88,11 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int q = 0; q < NQ; ++q)
-        bq[buf][j][q] = ld16((j < NH ? nb0 : nb1) + (j % NH) * kTileStride + i * kTileBytes + q * 1024);
+        bq[buf][j][q] = ld16((j < NH ? nb0 : nb1) + (j % NH) * kTileStride + i * KS * kTileBytes + q * 1024);
   };
   auto load_a = [&](int buf, int i) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[buf][q] = ld16(arow + i * 128 + 8 * q);
+    for (int q = 0; q < 4; ++q) a[buf][q] = ld16(arow + i * KS * 128 + 8 * q);
   };
 
   f32x4 acc[NT];
@@ -105,9 +112,9 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
   for (int i = 0; i < KTW; ++i) {
     if (i + 2 < KTW) load_b((i + 2) % 3, i + 2);
     __builtin_amdgcn_sched_barrier(0);
-    const int kt = kt0 + i;
+    const int kt = kt0 + i * KS;
     const int sh = 8 * (kt & 3);
-    const int d = KTW >= 4 ? (i >> 2) : 0;
+    const int d = IL ? i : (KTW >= 4 ? (i >> 2) : 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8 av = __builtin_bit_cast(bf16x8, a[i & 1][s]);

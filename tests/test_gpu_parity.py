@@ -370,25 +370,37 @@ def test_full_workloads(index, sample):
 
 # The largest batch the boundary accepts: MOE_MAX_TOKENS tokens on the
 # Zipf-skewed router of the 16384-token workload (the hottest expert takes
-# nearly every token, 4096 items of 64 rows).  7 * 262144 rows of H = 4096
-# put most element offsets into out_rows, h and the activations past 2^31.
-# Routing is checked on 1024 random tokens plus the first and the last,
+# nearly every token, 4096 items of 64 rows), for the default prefill path,
+# the scaled-FP4 option and 2-bit affine routed experts.  7 * 262144 rows of
+# H = 4096 put most element offsets into out_rows, h and the activations past
+# 2^31.  Routing is checked on 1024 random tokens plus the first and the last,
 # dispatch on every pair, expert rows and outputs on 4 tokens.
-def test_max_tokens():
+@pytest.mark.parametrize("path", ["mxfp4", "split_fp8", "affine2"])
+def test_max_tokens(path):
     w = WL.WORKLOADS[4]
     T = B.MOE_MAX_TOKENS
-    print(f"[parity] {w.name} router at T={T}", flush=True)
-    _, ex = _full_inputs(4)
-    inp = WL.make_layer_inputs(w, T=T, experts=_EXPERTS_CACHE[w.seed][0])
-    r = LC.full_check(inp, ex, sample_tokens=4, seed=7, route_sample=1024)
+    print(f"[parity] {w.name} router at T={T}, {path}", flush=True)
+    routed_fmt = "mxfp4"
+    if path == "affine2":
+        _EXPERTS_CACHE.clear()
+        canon = WL.make_experts_affine2(w.seed, WL.N_EXPERTS)
+        ex = B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, routed_affine2=True)
+        routed_fmt = "affine2"
+    else:
+        _, ex = _full_inputs(4)
+        canon = _EXPERTS_CACHE[w.seed][0]
+        if path == "split_fp8":
+            ex = B.Experts(ex.blob, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, split_fp8=True)
+    inp = WL.make_layer_inputs(w, T=T, experts=canon)
+    r = LC.full_check(inp, ex, sample_tokens=4, seed=7, route_sample=1024, routed_fmt=routed_fmt)
     off = r["g"]["offsets"]
     assert int(off[-1]) > (1 << 31) // WL.HIDDEN             # rows whose element offsets pass 2^31
     assert np.diff(off[: WL.N_EXPERTS + 1]).max() >= 0.98 * T
     sr = r["g"]["slot_row"][r["tokens"]]
     assert len(r["tokens"]) > 0 and (int(sr.max()) + 1) * WL.HIDDEN > 1 << 31   # checked rows past 2^31
-    print(f"[parity] T={T}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+    print(f"[parity] T={T} {path}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
-    del r, inp
+    del r, inp, ex
     torch.cuda.empty_cache()
 
 

@@ -7,12 +7,17 @@ synthetic inputs, already resident in HBM.  The expert blob is held in four
 copies at different addresses and the steps rotate through them, so the
 256 MB last-level cache cannot serve one step's expert bytes to the next.
 
-Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
-kernel (the expert gate/up launch: HBM-bound for the decode workloads, MFMA
-for prefill), timed with HIP events on the library's stream, and the CPU
-oracle timed on a bounded sample of the same workload.
+The default workload is the largest single-GPU configuration, the
+16384-token prefill with Zipf-skewed routing (MFMA bound); the 64-token decode
+batch (HBM bound) is timed in the same run and reported in a "decode"
+sub-object, so both halves of the metric come from one invocation.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode_t64]
+Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
+kernel (the expert gate/up launch: MFMA for prefill, HBM for decode), timed
+with HIP events on the library's stream, per-stage times, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill_t16384_zipf] [--decode-workload decode_t64]
 """
 from __future__ import annotations
 
@@ -39,7 +44,9 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_t64")
+    p.add_argument("--workload", default="prefill_t16384_zipf")
+    p.add_argument("--decode-workload", default="decode_t64",
+                   help="second workload timed in the same run and reported as the decode sub-object ('none': skip)")
     p.add_argument("--copies", type=int, default=4, help="expert blob copies rotated across steps")
     p.add_argument("--cpu-sample-tokens", type=int, default=40,
                    help="tokens of the workload the CPU oracle runs on (about 10-15 s of work)")
@@ -90,6 +97,11 @@ def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4", routed_fmt: str 
         cores = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
         cores = 1
+    host_cpus = os.cpu_count()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = host_cpus
     S = min(n_tokens, inp.x.shape[0])
     t0 = time.perf_counter()
     r = O.moe_layer(inp.x[:S], inp.experts, n_experts=inp.n_experts, hidden=inp.hidden, inter=inp.inter,
@@ -98,34 +110,21 @@ def cpu_baseline(inp, n_tokens: int, shared_fmt: str = "mxfp4", routed_fmt: str 
                     shared_fmt=shared_fmt, routed_fmt=routed_fmt)
     dt = time.perf_counter() - t0
     n_exp = int(np.count_nonzero(np.diff(r["offsets"])))
-    return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle",
+    return dict(value=S / dt, unit="tokens/s", cores=int(cores), kind="oracle", host_cpus=host_cpus,
+                affinity_cpus=affinity,
                 sample=f"first {S} of {inp.x.shape[0]} tokens of {inp.workload.name}: full layer, "
-                       f"{n_exp} experts decoded, {dt:.1f} s wall; float64 numpy, BLAS threads={cores}")
+                       f"{n_exp} experts decoded, {dt:.1f} s wall; float64 numpy on {cores} BLAS threads "
+                       f"(host: {host_cpus} CPUs, {affinity} in this process's affinity mask)")
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+STAGES = ("route", "dispatch", "ffn_plan", "ffn_gateup", "ffn_down", "combine")
 
-    import numpy as np
-    import torch
-    from mxfp4_routed_expert_moe_amd import binding as B
-    from mxfp4_routed_expert_moe_amd import workloads as WL
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    B.lib()  # fail loudly if the library is missing
-    wl = {w.name: w for w in WL.WORKLOADS}[args.workload]
+def measure(wl, args, B, WL, np, torch):
+    """Time K steps of the whole layer on workload wl (after W warm-up steps)
+    and return the figures of one JSON record (without the CPU baseline)."""
     print(f"[bench] workload {wl.name} T={wl.T}: generating inputs", file=sys.stderr, flush=True)
-    if args.ffn_split_fp8 and (args.shared_mxfp8 or args.routed_affine2):
-        print("--ffn-split-fp8 combines with neither --shared-mxfp8 nor --routed-affine2", file=sys.stderr)
-        sys.exit(2)
     shared_fmt = "mxfp8" if args.shared_mxfp8 else "mxfp4"
-    routed_fmt = "affine2" if args.routed_affine2 else "mxfp4"
     if args.routed_affine2:
         canon = WL.make_experts_affine2(wl.seed, WL.N_EXPERTS, shared=shared_fmt)
     elif args.shared_mxfp8:
@@ -166,27 +165,27 @@ def main():
     torch.cuda.synchronize()
 
     K, W = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # events on the library's stream (torch's current stream, which the
+    # binding passes to every call) between the launches of each stage
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(K)]
 
     def step(i, timed):
+        e = ev[i] if timed else None
         layer.set_experts(experts[i % len(experts)])
-        layer.route(x, tok)
-        layer.dispatch()
-        layer.expert_ffn_phase(x, 0)
+        calls = (lambda: layer.route(x, tok), layer.dispatch, lambda: layer.expert_ffn_phase(x, 0),
+                 lambda: layer.expert_ffn_phase(x, 1), lambda: layer.expert_ffn_phase(x, 2), layer.combine)
         if timed:
-            ev[i][0].record()
-        layer.expert_ffn_phase(x, 1)
-        if timed:
-            ev[i][1].record()
-        layer.expert_ffn_phase(x, 2)
-        if timed:
-            ev[i][2].record()
-        layer.combine()
+            e[0].record()
+        for j, c in enumerate(calls):
+            c()
+            if timed:
+                e[j + 1].record()
 
-    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: warmup {W} steps", file=sys.stderr, flush=True)
     for i in range(W):
         step(i, False)
     torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: timing {K} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(K):
         step(i, True)
@@ -195,8 +194,9 @@ def main():
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
     value = T * K / elapsed
-    gateup_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
-    down_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    stage_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]))
+                for j, name in enumerate(STAGES)}
+    gateup_ms = stage_ms["ffn_gateup"]
 
     # algorithmic work of the gate/up launch, from this run's own ids
     ids = layer.ids.cpu().numpy()
@@ -211,6 +211,7 @@ def main():
     shared_proj = H * I * 33 // 32 if args.shared_mxfp8 else mx4_proj
     gateup_bytes = (used - 1) * 2 * gate_proj + 2 * shared_proj + rows * H * 2 + rows * I * 2
     gateup_flops = rows * 2 * 2 * H * I
+    layer_flops = rows * 2 * 3 * H * I
     decode = rows <= 16 * (E + 1)
     if decode:
         achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
@@ -238,32 +239,80 @@ def main():
     roof["algorithmic_flops_per_launch"] = gateup_flops
 
     layer_bytes = (used - 1) * (2 * gate_proj + down_proj) + 3 * shared_proj
+    rec = dict(value=round(value, 1), ms_per_step=round(ms_per_step, 4), T=T, H=H, I=I, E=E, k=k,
+               used=used, rows=rows, layer_bytes=layer_bytes, roofline=roof, decode=decode,
+               layer_hbm_gbs=round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+               layer_mfma_tflops=round(layer_flops / (ms_per_step * 1e-3) / 1e12, 1),
+               stages_us={n: round(v * 1e3, 2) for n, v in stage_ms.items()}, inp=inp)
+    del layer, experts, blobs, blob0, x, tok
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mxfp4_routed_expert_moe_amd import binding as B
+    from mxfp4_routed_expert_moe_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()  # fail loudly if the library is missing
+    if args.ffn_split_fp8 and (args.shared_mxfp8 or args.routed_affine2):
+        print("--ffn-split-fp8 combines with neither --shared-mxfp8 nor --routed-affine2", file=sys.stderr)
+        sys.exit(2)
+    shared_fmt = "mxfp8" if args.shared_mxfp8 else "mxfp4"
+    routed_fmt = "affine2" if args.routed_affine2 else "mxfp4"
+    by_name = {w.name: w for w in WL.WORKLOADS}
+    wl = by_name[args.workload]
+    r = measure(wl, args, B, WL, np, torch)
+    inp = r.pop("inp")
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": r["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8x2-fp4" if (args.ffn_split_fp8 and not decode) else "bf16",
+        "dtype": "fp8x2-fp4" if (args.ffn_split_fp8 and not r["decode"]) else "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "hidden": H, "inter": I, "experts": E, "top_k": k,
-                   "routing": wl.routing, "bias": wl.bias,
+        "config": {"workload": wl.name, "tokens": r["T"], "hidden": r["H"], "inter": r["I"], "experts": r["E"],
+                   "top_k": r["k"], "routing": wl.routing, "bias": wl.bias,
                    "weights": ("affine 2-bit, bf16 (s, b) per 64/64/32" if args.routed_affine2
                                else "mxfp4 e2m1+e8m0/32"),
-                   "experts_read_per_step": used, "expert_bytes_per_step": layer_bytes,
-                   "blob_copies_rotated": len(experts),
+                   "experts_read_per_step": r["used"], "expert_bytes_per_step": r["layer_bytes"],
+                   "rows_per_step": r["rows"], "blob_copies_rotated": args.copies,
                    "ffn_prefill_arith": "split-fp8 scaled mfma" if args.ffn_split_fp8 else "bf16 mfma",
                    "shared_expert": shared_fmt},
-        "roofline": roof,
-        "layer_hbm_gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "stages_us": {"ffn_gateup": round(gateup_ms * 1e3, 2), "ffn_down": round(down_ms * 1e3, 2)},
+        "roofline": r["roofline"],
+        "layer_hbm_gbs": r["layer_hbm_gbs"],
+        "layer_mfma_tflops": r["layer_mfma_tflops"],
+        "layer_mfma_frac": round(r["layer_mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS, 4),
+        "stages_us": r["stages_us"],
+        "decode": None,
         "cpu_baseline": None,
     }
+    if args.decode_workload != "none" and args.decode_workload != wl.name:
+        d = measure(by_name[args.decode_workload], args, B, WL, np, torch)
+        d.pop("inp")
+        out["decode"] = {"workload": args.decode_workload, "tokens": d["T"], "value": d["value"],
+                         "unit": "tokens/s", "ms_per_step": d["ms_per_step"], "roofline": d["roofline"],
+                         "layer_hbm_gbs": d["layer_hbm_gbs"],
+                         "layer_hbm_frac": round(d["layer_hbm_gbs"] / HBM_PEAK_GBS, 4),
+                         "experts_read_per_step": d["used"], "expert_bytes_per_step": d["layer_bytes"],
+                         "stages_us": d["stages_us"]}
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_tokens, shared_fmt, routed_fmt)

@@ -352,14 +352,23 @@ def _full_inputs(index):
     return WL.make_layer_inputs(w, experts=canon), ex
 
 
+# Every full-size workload: routing on every token (bit-exact ids, no token
+# excused as a near tie), dispatch on every pair, every row and output written
+# (NaN-filled beforehand), whole experts against the oracle (the hottest, the
+# shared one, the smallest and eight whose row count is not a multiple of 64),
+# y of every token against the oracle's combine of the GPU's rows, and the
+# sampled tokens end to end.
 @pytest.mark.parametrize("index,sample", [(0, None), (1, 12), (2, 12), (3, 8), (4, 8)])
 def test_full_workloads(index, sample):
     w = WL.WORKLOADS[index]
     print(f"[parity] full workload {w.name} T={w.T}", flush=True)
     inp, ex = _full_inputs(index)
-    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, whole=8, y_all=True)
     print(f"[parity] {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
-          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}, ambiguous {r['ambiguous']}", flush=True)
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}, whole experts {r['whole_groups']} "
+          f"max/mean {r['whole_err'][0]:.2e}/{r['whole_err'][1]:.2e}, combine of all tokens "
+          f"{r['combine_err'][0]:.2e}/{r['combine_err'][1]:.2e}, ambiguous {r['ambiguous']}", flush=True)
+    assert r["ambiguous"] == 0
     if index == 4:
         counts = np.diff(r["g"]["offsets"][: WL.N_EXPERTS + 1])
         assert counts.max() >= 0.98 * w.T              # the hottest expert takes nearly every token
@@ -374,7 +383,9 @@ def test_full_workloads(index, sample):
 # the scaled-FP4 option and 2-bit affine routed experts.  7 * 262144 rows of
 # H = 4096 put most element offsets into out_rows, h and the activations past
 # 2^31.  Routing is checked on 1024 random tokens plus the first and the last,
-# dispatch on every pair, expert rows and outputs on 4 tokens.
+# dispatch on every pair, every row and output for being written (NaN-filled
+# beforehand), expert rows and outputs on 4 tokens, and every row of the
+# smallest expert and of four with a ragged last item.
 @pytest.mark.parametrize("path", ["mxfp4", "split_fp8", "affine2"])
 def test_max_tokens(path):
     w = WL.WORKLOADS[4]
@@ -392,7 +403,9 @@ def test_max_tokens(path):
         if path == "split_fp8":
             ex = B.Experts(ex.blob, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, split_fp8=True)
     inp = WL.make_layer_inputs(w, T=T, experts=canon)
-    r = LC.full_check(inp, ex, sample_tokens=4, seed=7, route_sample=1024, routed_fmt=routed_fmt)
+    r = LC.full_check(inp, ex, sample_tokens=4, seed=7, route_sample=1024, routed_fmt=routed_fmt, whole=4,
+                      whole_big=False)
+    assert r["ambiguous"] == 0
     off = r["g"]["offsets"]
     assert int(off[-1]) > (1 << 31) // WL.HIDDEN             # rows whose element offsets pass 2^31
     assert np.diff(off[: WL.N_EXPERTS + 1]).max() >= 0.98 * T
@@ -436,7 +449,8 @@ def test_split_fp8_full_prefill_workloads(index, sample):
     print(f"[parity] split fp8 full workload {w.name} T={w.T}", flush=True)
     inp, _ = _full_inputs(index)
     ex = B.Experts(_full_inputs(index)[1].blob, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, split_fp8=True)
-    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index)
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, whole=4, y_all=True)
+    assert r["ambiguous"] == 0
     print(f"[parity] split fp8 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r
@@ -511,7 +525,8 @@ def test_shared_mxfp8_full_workloads(index, sample):
     canon = WL.make_experts_shared_mxfp8(w.seed, WL.N_EXPERTS)
     inp = WL.make_layer_inputs(w, experts=canon)
     ex = B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, shared_mxfp8=True)
-    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, shared_fmt="mxfp8")
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, shared_fmt="mxfp8", whole=4, y_all=True)
+    assert r["ambiguous"] == 0
     print(f"[parity] shared mxfp8 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r, ex
@@ -582,7 +597,8 @@ def test_affine2_full_workloads(index, sample):
     canon = WL.make_experts_affine2(w.seed, WL.N_EXPERTS)
     inp = WL.make_layer_inputs(w, experts=canon)
     ex = B.Experts.from_canonical(canon, WL.N_EXPERTS, WL.HIDDEN, WL.INTER, routed_affine2=True)
-    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, routed_fmt="affine2")
+    r = LC.full_check(inp, ex, sample_tokens=sample, seed=index, routed_fmt="affine2", whole=4, y_all=True)
+    assert r["ambiguous"] == 0
     print(f"[parity] affine2 {w.name}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r, ex

@@ -213,6 +213,51 @@ def test_learned_routing_brute_force(bias_kind):
         assert abs(wt[t].sum() - 1.5) <= 1e-12
 
 
+def test_boundary_gap_hand_built_keys():
+    # A zero router gives every expert the same score sqrt(log 2); the
+    # selection keys are then that score plus a bias of exact binary
+    # fractions, so the gap between the k-th and (k+1)-th largest key is a
+    # difference of two biases, known in closed form (each key is one float64
+    # rounding of score + bias away from exact: 2^-52 at most).
+    E, H = 16, 512
+    x = WL.make_x(11, 3, H)
+    w = np.zeros((H, E), dtype=np.float32)
+    b = np.zeros(E, dtype=np.float32)
+    b[[4, 9, 1, 12, 2, 14, 7, 3]] = [1.0, 0.75, 0.5, 0.375, 0.25, 0.125, 0.0625, 0.03125]
+    # sorted biases: 1, .75, .5, .375, .25, .125 | .0625, .03125, 0 (x8)
+    for k, want in ((6, 0.125 - 0.0625), (3, 0.5 - 0.375), (1, 1.0 - 0.75), (8, 0.03125), (9, 0.0)):
+        gap = O.boundary_gap(x, w, b, k)
+        assert gap.shape == (3,)
+        assert np.all(np.abs(gap - want) <= 2.0 ** -50), (k, gap, want)
+    # an exact tie across the boundary: the 6th and 7th keys are equal
+    b2 = b.copy()
+    b2[7] = 0.125
+    assert np.all(O.boundary_gap(x, w, b2, 6) == 0.0)
+    # the gap is on the biased keys: without the bias every key is equal
+    assert np.all(O.boundary_gap(x, w, None, 6) == 0.0)
+
+
+@pytest.mark.parametrize("bias_kind", ["none", "random"])
+def test_boundary_gap_brute_force(bias_kind):
+    # keys from exactly summed logits and a 60-digit decimal sqrt-softplus,
+    # sorted in plain Python; the gap between the k-th and (k+1)-th largest
+    x, w = _small_routing_inputs()
+    E = w.shape[1]
+    bias = None if bias_kind == "none" else np.random.default_rng(9).standard_normal(E).astype(np.float32)
+    xf = O.bf16_bits_to_f64(x)
+    for k in (1, 6):
+        gap = O.boundary_gap(x, w, bias, k)
+        for t in range(0, x.shape[0], 3):
+            keys = []
+            for e in range(E):
+                z = math.fsum(float(xf[t, h]) * float(w[h, e]) for h in range(x.shape[1]))
+                keys.append(_dec_softplus_sqrt(z) + (0.0 if bias is None else float(bias[e])))
+            keys.sort(reverse=True)
+            want = keys[k - 1] - keys[k]
+            assert want > 0
+            assert abs(gap[t] - want) <= 1e-12 * max(1.0, abs(keys[0])), (k, t, gap[t], want)
+
+
 def test_selection_bias_only_selects():
     # +1e6 on six chosen experts forces exactly those; their weights still come
     # from the unbiased scores (selection bias changes choice, not weights).

@@ -283,6 +283,26 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
                  int32_t* slot_row, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, results and ordering as moe_dispatch without the
+ * workspace, whose contents (per-pair ranks, per-chunk counts) live instead
+ * in a static device array of MOE_DISPATCH_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call
+ * allocates nothing; its first call on a device looks up that device's array
+ * once (with the stream's device current).  A call whose scratch need
+ * (moe_dispatch_workspace_size(T, E, top_k)) exceeds the array returns
+ * MOE_EWORKSPACE and enqueues nothing: at E = 256 and top_k = 6 that is
+ * T > 149,000 or so.  Every word of the array a call reads it writes first,
+ * so the last call's contents never leak into the next; but all calls on one
+ * GPU share the array, so calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.
+ */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_dispatch_noalloc(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_t* offsets,
+                         int32_t* row_token, int32_t* slot_row, void* stream);
+
+/*
  * Expert FFN over every dispatched row ("Model techniques map --
  * DeepSeek-V4-Flash", row "SwiGLU feed-forward"; clamping also named in
  * "DeepSeek-V4-Flash export design", V3 reuse and V4 differences):

@@ -24,6 +24,7 @@ MOE_FFN_SPLIT_FP8 = 1  # moe_experts.flags: prefill expert FFN on the scaled FP4
 MOE_SHARED_MXFP8 = 2   # moe_experts.flags: the shared expert is MXFP8
 MOE_ROUTED_AFFINE2 = 4  # moe_experts.flags: the routed experts are 2-bit affine (JANG recipe)
 MOE_MAX_TOKENS = 262144  # largest T any call accepts
+MOE_DISPATCH_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of moe_dispatch_noalloc, per GPU
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "MOE_ESHAPE",
           5: "MOE_EWORKSPACE", 6: "MOE_EHIP"}
 
@@ -31,7 +32,8 @@ EXPORTED = ("moe_status_str", "moe_abi_version", "moe_expert_bytes", "moe_expert
             "moe_unpack_mxfp4", "moe_expert_bytes_mxfp8", "moe_pack_mxfp8", "moe_unpack_mxfp8",
             "moe_expert_bytes_affine2", "moe_pack_affine2", "moe_unpack_affine2", "moe_route_workspace_size", "moe_route",
             "moe_dispatch_workspace_size",
-            "moe_dispatch", "moe_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_phase", "moe_combine")
+            "moe_dispatch", "moe_dispatch_noalloc", "moe_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_phase",
+            "moe_combine")
 
 
 class MoeError(RuntimeError):
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
                                      vp, vp, vp, c_sz, vp]),
         "moe_dispatch_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
         "moe_dispatch": (ctypes.c_int, [vp, c_i32, c_i32, c_i32, vp, vp, vp, vp, c_sz, vp]),
+        "moe_dispatch_noalloc": (ctypes.c_int, [vp, c_i32, c_i32, c_i32, vp, vp, vp, vp]),
         "moe_ffn_workspace_size": (c_sz, [c_i32, ctypes.POINTER(moe_experts), c_i32]),
         "moe_expert_ffn": (ctypes.c_int, [vp, c_i32, ctypes.POINTER(moe_experts), c_i32, vp, vp, ctypes.c_float,
                                           vp, vp, c_sz, vp]),
@@ -258,6 +261,21 @@ def dispatch(ids, E: int):
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     _check("moe_dispatch", lib().moe_dispatch(_ptr(ids), T, E, k, _ptr(offsets), _ptr(row_token), _ptr(slot_row),
                                               _ptr(ws), ws.numel(), _stream()))
+    return offsets, row_token, slot_row
+
+
+def dispatch_noalloc(ids, E: int, offsets=None, row_token=None, slot_row=None):
+    """moe_dispatch_noalloc (no workspace): the outputs of dispatch(), written
+    into the given tensors or new ones."""
+    torch = _torch()
+    _dev(ids, torch.int32, "ids")
+    T, k = ids.shape
+    dev = ids.device
+    offsets = torch.empty(E + 2, dtype=torch.int32, device=dev) if offsets is None else offsets
+    row_token = torch.empty(T * (k + 1), dtype=torch.int32, device=dev) if row_token is None else row_token
+    slot_row = torch.empty((T, k + 1), dtype=torch.int32, device=dev) if slot_row is None else slot_row
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(_ptr(ids), T, E, k, _ptr(offsets), _ptr(row_token),
+                                                              _ptr(slot_row), _stream()))
     return offsets, row_token, slot_row
 
 

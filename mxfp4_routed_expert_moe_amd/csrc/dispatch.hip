@@ -13,7 +13,18 @@
 //     pair's row = offsets[e] + chunk base + rank, and the shared rows.
 // Small batches (T * k <= 2048, E <= 256) take one single-block kernel with
 // the same result (ranks from wave ballots and per-chunk prefix counts).
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Scratch of moe_dispatch_noalloc: the per-pair ranks and per-chunk counts
+// that moe_dispatch keeps in its workspace argument, in a static device array
+// instead (every GPU the library runs on holds its own copy until the process
+// ends).  Host code never passes this name to a kernel: it is a host-side
+// stand-in for the device symbol.  Its device address, per device, comes from
+// hipGetSymbolAddress (dispatch_noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_DISPATCH_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 
@@ -208,6 +219,38 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
   }
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of `scratch` on the device that owns stream s (the
+// current device for the null stream), looked up once per device with that
+// device current and kept for later calls.
+hipError_t dispatch_noalloc_scratch(hipStream_t s, void** out) {
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && (e = hipSetDevice(cur)) != hipSuccess) return e;
+      if (eg != hipSuccess) return eg;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 size_t dispatch_ws_bytes(int T, int E, int k) {
@@ -228,6 +271,16 @@ hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* off
   dispatch_chunk_scan_kernel<<<E, 64, 0, s>>>(nch, w);
   dispatch_scatter_kernel<<<nch, 256, 0, s>>>(ids, T, E, k, nch, w, offsets, row_token, slot_row);
   return hipGetLastError();
+}
+
+hipError_t launch_dispatch_noalloc(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
+                                   int32_t* slot_row, hipStream_t s) {
+  // Every word of the scratch the kernels read is written earlier in the same
+  // call, so nothing needs clearing between calls.
+  void* ws = nullptr;
+  const hipError_t e = dispatch_noalloc_scratch(s, &ws);
+  if (e != hipSuccess) return e;
+  return launch_dispatch(ids, T, E, k, offsets, row_token, slot_row, ws, s);
 }
 
 }  // namespace moe

@@ -114,6 +114,17 @@ int moe_dispatch(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_
   return hip_status(moe::launch_dispatch(ids, T, E, top_k, offsets, row_token, slot_row, ws, as_stream(stream)));
 }
 
+int moe_dispatch_noalloc(const int32_t* ids, int32_t T, int32_t E, int32_t top_k, int32_t* offsets,
+                         int32_t* row_token, int32_t* slot_row, void* stream) {
+  if (T < 0) return MOE_EINVAL;
+  if (T > kMaxTokens) return MOE_ESHAPE;
+  if (top_k < 1 || top_k > kMaxTopK || E < 1 || E > kMaxExperts) return MOE_ESHAPE;
+  if (T == 0) return MOE_OK;
+  if (!ids || !offsets || !row_token || !slot_row) return MOE_EINVAL;
+  if (moe::dispatch_ws_bytes(T, E, top_k) > MOE_DISPATCH_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  return hip_status(moe::launch_dispatch_noalloc(ids, T, E, top_k, offsets, row_token, slot_row, as_stream(stream)));
+}
+
 size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k) {
   if (T <= 0 || T > kMaxTokens || top_k < 1 || top_k > kMaxTopK || check_experts(experts) != MOE_OK) return 0;
   return moe::ffn_ws_bytes(T, experts->n_experts, experts->hidden, experts->inter, top_k,

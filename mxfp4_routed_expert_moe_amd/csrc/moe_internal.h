@@ -203,6 +203,9 @@ hipError_t launch_route_hash(const int32_t* tok, int T, const int32_t* table, in
 size_t dispatch_ws_bytes(int T, int E, int k);
 hipError_t launch_dispatch(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
                            int32_t* slot_row, void* ws, hipStream_t s);
+// The same with the library's static scratch (moe_dispatch_noalloc).
+hipError_t launch_dispatch_noalloc(const int32_t* ids, int T, int E, int k, int32_t* offsets, int32_t* row_token,
+                                   int32_t* slot_row, hipStream_t s);
 
 // split_fp8: the prefill family on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8);
 // shared_w8: the shared expert is MXFP8 (MOE_SHARED_MXFP8); routed_a2: the

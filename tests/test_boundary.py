@@ -249,6 +249,29 @@ def test_dispatch_checks():
     assert need > 0 and _dispatch(ws_bytes=need - 1) == EWORKSPACE
 
 
+def _dispatch_noalloc(T=64, E=256, k=6, ids=FAKE, off=FAKE, rt=FAKE, sr=FAKE):
+    v = lambda p: None if p is None else ctypes.c_void_p(p)  # noqa: E731
+    return B.lib().moe_dispatch_noalloc(v(ids), T, E, k, v(off), v(rt), v(sr), None)
+
+
+def test_dispatch_noalloc_checks():
+    # refused calls return before any HIP call: no GPU needed
+    assert _dispatch_noalloc(T=0) == OK
+    assert _dispatch_noalloc(T=-3) == EINVAL
+    assert _dispatch_noalloc(T=B.MOE_MAX_TOKENS + 1) == ESHAPE
+    assert _dispatch_noalloc(k=9) == ESHAPE and _dispatch_noalloc(E=0) == ESHAPE
+    for name in ("ids", "off", "rt", "sr"):
+        assert _dispatch_noalloc(**{name: None}) == EINVAL
+    # the static scratch holds what moe_dispatch's workspace would: calls
+    # needing more are refused with MOE_EWORKSPACE
+    cap = B.MOE_DISPATCH_NOALLOC_SCRATCH_BYTES
+    L = B.lib()
+    T_ok = max(T for T in range(140000, 160000, 64) if L.moe_dispatch_workspace_size(T, 256, 6) <= cap)
+    assert T_ok > 140000
+    assert _dispatch_noalloc(T=T_ok + 64) == EWORKSPACE
+    assert _dispatch_noalloc(T=100000, E=1023, k=8) == EWORKSPACE
+
+
 def _ffn(T=64, d=None, k=6, x=FAKE, off=FAKE, rt=FAKE, L=10.0, out=FAKE, ws=FAKE, ws_bytes=1 << 40):
     v = lambda p: None if p is None else ctypes.c_void_p(p)  # noqa: E731
     d = _desc() if d is None else d

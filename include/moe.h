@@ -9,7 +9,7 @@
  *
  *   moe_route       x -> (ids [T,k], weights [T,k])
  *   moe_dispatch    ids -> (offsets, row_token, slot_row)
- *   moe_expert_ffn  x, packed MXFP4 experts -> out_rows [rows, H] (float32)
+ *   moe_expert_ffn  x, packed MXFP4 experts -> out_rows [rows, H] (bf16)
  *   moe_combine     out_rows, slot_row, weights -> y [T, H] (bf16)
  *
  * Conventions shared by every call:
@@ -308,7 +308,7 @@ int moe_dispatch_noalloc(const int32_t* ids, int32_t T, int32_t E, int32_t top_k
  * "DeepSeek-V4-Flash export design", V3 reuse and V4 differences):
  *   g = W_gate[e] x,  u = W_up[e] x                  (float32 accumulation)
  *   h = bf16( silu(min(g, L)) * min(max(u, -L), L) )
- *   out_rows[p] = W_down[e] h                        (float32 accumulation)
+ *   out_rows[p] = bf16( W_down[e] h )                (float32 accumulation)
  * for each row p of group e, x = x[row_token[p]].  The MXFP4 weights are
  * decoded to bf16 on the fly and fed to bf16 MFMA (or, with MOE_FFN_SPLIT_FP8
  * in experts->flags and a prefill-sized T, fed as stored to the scaled FP4
@@ -319,13 +319,15 @@ int moe_dispatch_noalloc(const int32_t* ids, int32_t T, int32_t E, int32_t top_k
  *
  * x         bf16 [T, H]; experts: descriptor (host pointer) of the device blob
  * offsets, row_token: as written by moe_dispatch for the same T, E, top_k
- * out_rows  float32 [T * (top_k + 1), H] out (rows past offsets[E+1] untouched)
+ * out_rows  bf16 [T * (top_k + 1), H] out, 16-byte aligned (rows past
+ *           offsets[E+1] untouched); each row rounded once (to nearest even)
+ *           from its float32 sum, activations in bf16 as x and h are
  * ws        at least moe_ffn_workspace_size(T, experts, top_k) bytes, 256-byte aligned
  * clamp_limit L > 0.
  */
 size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top_k);
 int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
-                   const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
+                   const int32_t* offsets, const int32_t* row_token, float clamp_limit, uint16_t* out_rows,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -337,8 +339,8 @@ int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int
  * call bit for bit.  phase -1 runs all three; any other value is MOE_EINVAL.
  */
 int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
-                         const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
-                         void* ws, size_t ws_bytes, int32_t phase, void* stream);
+                         const int32_t* offsets, const int32_t* row_token, float clamp_limit,
+                         uint16_t* out_rows, void* ws, size_t ws_bytes, int32_t phase, void* stream);
 
 /*
  * Weighted combine plus the shared expert ("Model techniques map --
@@ -348,10 +350,10 @@ int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* expert
  * summed in float32 in that fixed order (the deterministic reduction the
  * techniques map lists under inference kernels).  slot_row entries of -1 are
  * skipped.
- * out_rows float32 [rows, H]; slot_row int32 [T, top_k+1]; weights float32
+ * out_rows bf16 [rows, H]; slot_row int32 [T, top_k+1]; weights float32
  * [T, top_k]; y bf16 [T, H] out.  H a positive multiple of 8.
  */
-int moe_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
+int moe_combine(const uint16_t* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
                 int32_t top_k, uint16_t* y, void* stream);
 
 #ifdef __cplusplus

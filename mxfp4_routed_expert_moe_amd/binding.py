@@ -284,12 +284,12 @@ def ffn_workspace_size(T: int, experts: Experts, top_k: int) -> int:
 
 
 def expert_ffn(x, experts: Experts, top_k: int, offsets, row_token, clamp_limit: float, out_rows=None, ws=None):
-    """moe_expert_ffn -> out_rows float32 [T*(k+1), H]."""
+    """moe_expert_ffn -> out_rows bf16 [T*(k+1), H]."""
     torch = _torch()
     T = x.shape[0]
     H = experts.hidden
     if out_rows is None:
-        out_rows = torch.empty((T * (top_k + 1), H), dtype=torch.float32, device=x.device)
+        out_rows = torch.empty((T * (top_k + 1), H), dtype=torch.bfloat16, device=x.device)
     if ws is None:
         ws = torch.empty(max(ffn_workspace_size(T, experts, top_k), 1), dtype=torch.uint8, device=x.device)
     _check("moe_expert_ffn", lib().moe_expert_ffn(_ptr(x), T, ctypes.byref(experts.desc), top_k, _ptr(offsets),
@@ -326,7 +326,7 @@ class MoeLayer:
         self.offsets = torch.empty(E + 2, dtype=torch.int32, device=dev)
         self.row_token = torch.empty(T * (k + 1), dtype=torch.int32, device=dev)
         self.slot_row = torch.empty((T, k + 1), dtype=torch.int32, device=dev)
-        self.out_rows = torch.empty((T * (k + 1), H), dtype=torch.float32, device=dev)
+        self.out_rows = torch.empty((T * (k + 1), H), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((T, H), dtype=torch.int16, device=dev)
         L = lib()
         self.ws_route = torch.empty(max(int(L.moe_route_workspace_size(T, H, E)), 256), dtype=torch.uint8, device=dev)

@@ -5,7 +5,7 @@
 // A plain gather-reduce in a fixed order -- no atomics -- so the output is
 // bit-reproducible (the deterministic reductions listed among the inference
 // kernels of the same page).  HBM bound: each thread owns 8 columns of one
-// token, reads 7 rows of 32 bytes and writes 16 bytes.
+// token, reads 7 bf16 rows of 16 bytes and writes 16 bytes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -13,9 +13,9 @@ namespace moe {
 namespace {
 
 // All row indices and weights of a token are read first, then all of its
-// row loads are issued together, so a thread waits for one memory round
-// trip, not one per slot.
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ out_rows,
+// row loads are issued together (16 bytes = 8 bf16 columns each), so a
+// thread waits for one memory round trip, not one per slot.
+__global__ __launch_bounds__(128) void combine_kernel(const uint16_t* __restrict__ out_rows,
                                                       const int32_t* __restrict__ slot_row,
                                                       const float* __restrict__ weights, int T, int H, int k,
                                                       uint16_t* __restrict__ y) {
@@ -34,18 +34,15 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     w[j] = j < k ? weights[static_cast<size_t>(t) * k + j] : 0.f;
   }
   rows[kMaxK] = sr[k];
-  f32x4 v[kMaxK + 1][2];
+  u32x4 v[kMaxK + 1];
 #pragma unroll
-  for (int j = 0; j <= kMaxK; ++j) {
-    if (rows[j] >= 0) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(out_rows + static_cast<size_t>(rows[j]) * H + c);
-      v[j][0] = p[0];
-      v[j][1] = p[1];
-    } else {
-      v[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      v[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
+  for (int j = 0; j <= kMaxK; ++j)
+    v[j] = rows[j] >= 0 ? ld16(out_rows + static_cast<size_t>(rows[j]) * H + c) : u32x4{0u, 0u, 0u, 0u};
+  // element 2i of a row is the low half of word i, element 2i + 1 the high half
+  auto elem = [&](const u32x4& r, int e) {
+    const uint32_t word = r[e >> 1];
+    return __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+  };
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -53,16 +50,10 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < kMaxK; ++j) {
     if (rows[j] < 0) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = fmaf(w[j], v[j][0][i], acc[i]);
-      acc[4 + i] = fmaf(w[j], v[j][1][i], acc[4 + i]);
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], elem(v[j], i), acc[i]);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[i] += v[kMaxK][0][i];
-    acc[4 + i] += v[kMaxK][1][i];
-  }
+  for (int i = 0; i < 8; ++i) acc[i] += elem(v[kMaxK], i);
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -73,7 +64,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
+hipError_t launch_combine(const uint16_t* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s) {
   const long threads = static_cast<long>(T) * (H / 8);
   combine_kernel<<<static_cast<unsigned>((threads + 127) / 128), 128, 0, s>>>(out_rows, slot_row, weights, T, H, k, y);

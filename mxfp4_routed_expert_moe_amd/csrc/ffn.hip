@@ -110,7 +110,7 @@ size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool rout
 }
 
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
-                      int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
+                      int k, const int32_t* offsets, const int32_t* row_token, float limit, uint16_t* out_rows,
                       void* ws, int phase, bool split_fp8, bool shared_w8, bool routed_a2, hipStream_t s) {
   const int bm = ffn_bm(T, E, k, H, I);
   const int max_items = ffn_max_items(T, E, k, bm);

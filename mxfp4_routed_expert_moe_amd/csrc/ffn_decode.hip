@@ -24,7 +24,7 @@ template <bool GATEUP, int KTW, bool W8>
 __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
                                              int g, int row0, int nrows, const uint8_t* __restrict__ blob,
                                              uint64_t expert_bytes, int H, int I, float limit,
-                                             uint16_t* __restrict__ h_out, float* __restrict__ out_rows,
+                                             uint16_t* __restrict__ h_out, uint16_t* __restrict__ out_rows,
                                              f32x4 (*red)[8][64]) {
   constexpr int KT = kWaves * KTW;    // k tiles of the whole K axis
   constexpr int NT = W8 ? 4 : 8;      // n-tiles per block (GATEUP: NT/2 gate + NT/2 up)
@@ -179,7 +179,7 @@ __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, c
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = rbase + e;
-        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = os[e];
+        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = float_to_bf16_bits(os[e]);
       }
     }
   }
@@ -213,7 +213,7 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
                                                 const int32_t* __restrict__ row_token, int g, int row0, int nrows,
                                                 const uint8_t* __restrict__ blob, uint64_t expert_bytes, int H,
                                                 int I, float limit, uint16_t* __restrict__ h_out,
-                                                float* __restrict__ out_rows, f32x4 (*red)[8][64]) {
+                                                uint16_t* __restrict__ out_rows, f32x4 (*red)[8][64]) {
   constexpr int KT = kWaves * KTW;
   constexpr int NT = 8;
   constexpr int NH = NT / 2;
@@ -365,7 +365,7 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = rbase + e;
-        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = os[e];
+        if (rr < nrows) out_rows[static_cast<size_t>(row0 + rr) * H + col] = float_to_bf16_bits(os[e]);
       }
     }
   }
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
                                                             const int32_t* __restrict__ offsets, int E, int nrouted,
                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
                                                             int H, int I, float limit, uint16_t* __restrict__ h_out,
-                                                            float* __restrict__ out_rows) {
+                                                            uint16_t* __restrict__ out_rows) {
   int g, first, end;
   if (static_cast<int>(blockIdx.y) < nrouted) {
     g = blockIdx.y;
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
 
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
                        int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
-                       float* out_rows, bool shared_w8, bool routed_a2, hipStream_t s) {
+                       uint16_t* out_rows, bool shared_w8, bool routed_a2, hipStream_t s) {
   const int K = gateup ? H : I;
   const int ktw = K / (128 * kWaves);  // k tiles per wave; decode_k_ok(K) keeps it in {1, 2, 4, 8}
   if (ktw * 128 * kWaves != K) return;  // never taken: decode_k_ok(K) holds for the decode path
@@ -447,7 +447,7 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
   const dim3 grid(nb, E + (shared_w8 ? 0 : chunks));
   const dim3 grid_sh(nb8, chunks);
   uint16_t* ho = gateup ? h : nullptr;
-  float* oo = gateup ? nullptr : out_rows;
+  uint16_t* oo = gateup ? nullptr : out_rows;
 #define MOE_DECODE_LAUNCH(G, KTW)                                                                                 \
   do {                                                                                                          \
     if (routed_a2)                                                                                              \

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
                                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes,
                                                              int H, int I, float limit, int skip_g, int n_tail,
                                                              uint16_t* __restrict__ h_out,
-                                                             float* __restrict__ out_rows) {
+                                                             uint16_t* __restrict__ out_rows) {
   constexpr bool W8 = FMT == kFmtMx8;
   constexpr bool A2 = FMT == kFmtA2;
   constexpr int kNT = kNT4;           // weight n-tiles per wave
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
-          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = acc[mt][j][e];
+          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = float_to_bf16_bits(acc[mt][j][e]);
         }
       }
     }
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 }  // namespace
 
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
-                        const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows, int max_items,
+                        const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows, int max_items,
                         int T, int E, bool shared_w8, bool routed_a2, hipStream_t s) {
   // The routed experts' launch (MXFP4, with an MXFP4 shared expert riding
   // along, or 2-bit affine), then the shared expert's own launch over the last
@@ -363,7 +363,7 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   const int ny = max_items + kGridSlack, ny_sh = nsh + kGridSlack;
   const dim3 grid(gateup ? I / 128 : H / 256, ny), grid_sh(gateup ? I / 128 : H / 256, ny_sh);
   uint16_t* ho = gateup ? w.h : nullptr;
-  float* oo = gateup ? nullptr : out_rows;
+  uint16_t* oo = gateup ? nullptr : out_rows;
   const int32_t* rt = gateup ? row_token : nullptr;
 #define MOE_PREFILL(G)                                                                                            \
   do {                                                                                                          \

@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_f8_kernel(QAct aq, co
                                                                  const int32_t* __restrict__ n_items,
                                                                  const uint8_t* __restrict__ blob,
                                                                  uint64_t expert_bytes, int H, int I, float limit,
-                                                                 QAct hq, float* __restrict__ out_rows) {
+                                                                 QAct hq, uint16_t* __restrict__ out_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages][kStageBytes];
   const int nbc = gridDim.x;
   const int total = *n_items * nbc;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_f8_kernel(QAct aq, co
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rbase + e;
-          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = acc[mt][j][e];
+          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = float_to_bf16_bits(acc[mt][j][e]);
         }
       }
     }
@@ -321,7 +321,7 @@ void launch_quant_act(const uint16_t* src, int rows, int K, const QAct& dst, hip
 }
 
 void launch_ffn_prefill_f8(bool gateup, const QAct& aq, const int32_t* row_token, const FfnWs& w,
-                           const uint8_t* blob, uint64_t eb, int H, int I, float limit, float* out_rows,
+                           const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows,
                            int max_items, hipStream_t s) {
   if (gateup) {
     dim3 g1(I / 128, max_items + kGridSlack);

@@ -134,7 +134,7 @@ size_t moe_ffn_workspace_size(int32_t T, const moe_experts* experts, int32_t top
 namespace {
 
 int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k, const int32_t* offsets,
-             const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes, int32_t phase,
+             const int32_t* row_token, float clamp_limit, uint16_t* out_rows, void* ws, size_t ws_bytes, int32_t phase,
              void* stream) {
   if (T < 0) return MOE_EINVAL;
   if (T > kMaxTokens) return MOE_ESHAPE;
@@ -157,18 +157,18 @@ int ffn_call(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t t
 }  // namespace
 
 int moe_expert_ffn(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k, const int32_t* offsets,
-                   const int32_t* row_token, float clamp_limit, float* out_rows, void* ws, size_t ws_bytes,
+                   const int32_t* row_token, float clamp_limit, uint16_t* out_rows, void* ws, size_t ws_bytes,
                    void* stream) {
   return ffn_call(x, T, experts, top_k, offsets, row_token, clamp_limit, out_rows, ws, ws_bytes, -1, stream);
 }
 
 int moe_expert_ffn_phase(const uint16_t* x, int32_t T, const moe_experts* experts, int32_t top_k,
-                         const int32_t* offsets, const int32_t* row_token, float clamp_limit, float* out_rows,
+                         const int32_t* offsets, const int32_t* row_token, float clamp_limit, uint16_t* out_rows,
                          void* ws, size_t ws_bytes, int32_t phase, void* stream) {
   return ffn_call(x, T, experts, top_k, offsets, row_token, clamp_limit, out_rows, ws, ws_bytes, phase, stream);
 }
 
-int moe_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
+int moe_combine(const uint16_t* out_rows, const int32_t* slot_row, const float* weights, int32_t T, int32_t H,
                 int32_t top_k, uint16_t* y, void* stream) {
   if (T < 0) return MOE_EINVAL;
   if (T > kMaxTokens) return MOE_ESHAPE;

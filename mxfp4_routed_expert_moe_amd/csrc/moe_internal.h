@@ -212,10 +212,10 @@ hipError_t launch_dispatch_noalloc(const int32_t* ids, int T, int E, int k, int3
 // routed experts are 2-bit affine (MOE_ROUTED_AFFINE2).
 size_t ffn_ws_bytes(int T, int E, int H, int I, int k, bool split_fp8, bool routed_a2);
 hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t expert_bytes, int E, int H, int I,
-                      int k, const int32_t* offsets, const int32_t* row_token, float limit, float* out_rows,
+                      int k, const int32_t* offsets, const int32_t* row_token, float limit, uint16_t* out_rows,
                       void* ws, int phase, bool split_fp8, bool shared_w8, bool routed_a2, hipStream_t s);
 
-hipError_t launch_combine(const float* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
+hipError_t launch_combine(const uint16_t* out_rows, const int32_t* slot_row, const float* weights, int T, int H, int k,
                           uint16_t* y, hipStream_t s);
 
 }  // namespace moe

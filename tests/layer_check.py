@@ -26,6 +26,11 @@ def dev(a: np.ndarray):
 
 
 def host(t) -> np.ndarray:
+    """Host copy of a device tensor; bf16 tensors (the expert rows) come back
+    as their exact float64 values."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
     return t.cpu().numpy()
 
 

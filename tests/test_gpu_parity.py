@@ -169,6 +169,9 @@ def test_identity_experts_closed_form_and_orientation(T, split):
         # allow 2^-18 of the 32-column block maximum.
         blk = np.repeat(np.abs(want).reshape(want.shape[0], I // 32, 32).max(axis=2), 32, axis=1)
         tol = tol + 2.0 ** -18 * blk
+        # the expert row is rounded to bf16 once more (half an ulp, 2^-9
+        # relative), no longer exactly h once the split has moved it
+        tol = tol + 2.0 ** -9 * np.abs(rows[:, :I])
     assert np.all(np.abs(rows[:, :I] - want) <= tol)
     assert np.all(rows[:, I:] == 0)
     swapped = silu(np.minimum(2 * v, L)) * np.clip(v, -L, L)

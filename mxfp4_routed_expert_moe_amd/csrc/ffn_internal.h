@@ -34,6 +34,28 @@ constexpr int kPrefillRows = 64;   // rows per prefill item
 // reaches every logical block only with at least 8 * ceil(n / 8) blocks.
 constexpr int kGridSlack = 7;
 
+// Traversal of a prefill grid of n_items x nbc (item, column block) units:
+// logical unit lam belongs to the window of kWinItems consecutive items
+// (the last window may hold fewer) x kWinCb consecutive column blocks, and
+// walks it column block fastest.  The units of one XCD are consecutive
+// logical units, so the ~64 blocks an XCD runs at once cover one window: an
+// expert's weight slice of a column block is shared by the window's items of
+// that expert and an item's activation rows by its column blocks, both
+// streamed through one L2 by blocks that start together.
+constexpr int kWinItems = 8, kWinCb = 8;
+
+__device__ __forceinline__ void window_unit(int lam, int n_items, int nbc, int& item, int& cb) {
+  const int gc = nbc % kWinCb == 0 ? kWinCb : 1;
+  const int per_group = kWinItems * nbc;
+  const int ig = lam / per_group;
+  const int r = lam - ig * per_group;
+  const int ni = min(kWinItems, n_items - ig * kWinItems);
+  const int cg = r / (ni * gc);
+  const int r2 = r - cg * ni * gc;
+  item = ig * kWinItems + r2 / gc;
+  cb = cg * gc + r2 % gc;
+}
+
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
 // expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
 template <int N>

@@ -36,10 +36,11 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 // in flight while kt and kt+1 are multiplied; one barrier per pair halves the
 // block-wide synchronisation.
 //
-// Block order is remapped so the n blocks of one item run on the same XCD:
+// Block order is remapped so consecutive logical blocks run on the same XCD:
 // blocks go to the 8 XCDs round robin, and block b takes logical work
-// b % 8 * ceil(total / 8) + b / 8, so consecutive logical blocks (the column
-// blocks of one item, then the next item of the same expert) share an L2.
+// b % 8 * ceil(total / 8) + b / 8; logical blocks walk windows of items x
+// column blocks (window_unit), so the blocks an XCD runs at once share
+// weight slices and activation rows in its L2.
 // That covers every logical block only if the grid has at least
 // 8 * ceil(total / 8) blocks: launches add kGridSlack rows of blocks.
 //
@@ -87,8 +88,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   if ((b >> 3) >= per) return;
   const int lam = (b & 7) * per + (b >> 3);
   if (lam >= total) return;
-  const int4 it = items[(n_tail > 0 ? nit - n_tail : 0) + lam / nbc];
-  const int nb = lam % nbc;
+  int item, nb;
+  window_unit(lam, n_tail > 0 ? n_tail : nit, nbc, item, nb);
+  const int4 it = items[(n_tail > 0 ? nit - n_tail : 0) + item];
   const int g = it.x, row0 = it.y, nrows = it.z;
   if (g == skip_g) return;  // this group's items run in a launch of their own
   const int K = GATEUP ? H : I;

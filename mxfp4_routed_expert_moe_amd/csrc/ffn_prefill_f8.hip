@@ -114,14 +114,16 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_f8_kernel(QAct aq, co
                                                                  QAct hq, uint16_t* __restrict__ out_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages][kStageBytes];
   const int nbc = gridDim.x;
-  const int total = *n_items * nbc;
+  const int nit = *n_items;
+  const int total = nit * nbc;
   const int b = blockIdx.x + blockIdx.y * nbc;
   const int per = (total + 7) >> 3;
   if ((b >> 3) >= per) return;
   const int lam = (b & 7) * per + (b >> 3);
   if (lam >= total) return;
-  const int4 it = items[lam / nbc];
-  const int nb = lam % nbc;
+  int item, nb;
+  window_unit(lam, nit, nbc, item, nb);
+  const int4 it = items[item];
   const int g = it.x, row0 = it.y, nrows = it.z;
   const int K = GATEUP ? H : I;
   const int KT = K >> 7;  // a multiple of 4

@@ -92,6 +92,9 @@ extern "C" {
  */
 #define MOE_ROUTED_AFFINE2 4
 
+/* Largest hidden or intermediate size (H, I) any call accepts. */
+#define MOE_MAX_DIM 65536
+
 /* Largest token count T any call accepts (MOE_ESHAPE beyond; the workspace
  * size queries return 0): it keeps every launch's grid within the device's
  * limits and every row count T * (top_k + 1) in 32 bits. */
@@ -180,7 +183,8 @@ typedef struct moe_experts {
 } moe_experts;
 
 /* Bytes of one expert (gate + up + down) of shape (H, I): 3*H*I*17/32.
- * Returns 0 for unsupported shapes (H, I must be positive multiples of 512). */
+ * Returns 0 for unsupported shapes (H, I must be positive multiples of 512,
+ * at most MOE_MAX_DIM). */
 uint64_t moe_expert_bytes(int32_t hidden, int32_t inter);
 
 /* Fill a descriptor for a device blob in MOE_LAYOUT_GFX950_TILED_V1.
@@ -255,7 +259,8 @@ int moe_unpack_affine2(const uint8_t* src_device_layout, uint64_t src_bytes, int
  * ids      int32 [T, top_k] out;  weights float32 [T, top_k] out
  * ws       device workspace of at least moe_route_workspace_size(T, H, E) bytes,
  *          256-byte aligned (learned mode; may be NULL in hash mode)
- * Requirements: 1 <= top_k <= 8, top_k <= E <= 256, H a positive multiple of 512.
+ * Requirements: 1 <= top_k <= 8, top_k <= E <= 256, H a positive multiple of
+ * 512 up to MOE_MAX_DIM (MOE_ESHAPE otherwise).
  */
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E);
 int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, const float* sel_bias,

@@ -24,6 +24,7 @@ MOE_FFN_SPLIT_FP8 = 1  # moe_experts.flags: prefill expert FFN on the scaled FP4
 MOE_SHARED_MXFP8 = 2   # moe_experts.flags: the shared expert is MXFP8
 MOE_ROUTED_AFFINE2 = 4  # moe_experts.flags: the routed experts are 2-bit affine (JANG recipe)
 MOE_MAX_TOKENS = 262144  # largest T any call accepts
+MOE_MAX_DIM = 65536  # largest H or I any call accepts
 MOE_DISPATCH_NOALLOC_SCRATCH_BYTES = 8 << 20  # static scratch of moe_dispatch_noalloc, per GPU
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EALIGN", 3: "MOE_ELAYOUT", 4: "MOE_ESHAPE",
           5: "MOE_EWORKSPACE", 6: "MOE_EHIP"}

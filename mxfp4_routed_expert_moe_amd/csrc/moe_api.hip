@@ -69,7 +69,7 @@ int moe_experts_init(moe_experts* d, const void* base, int32_t n_experts, int32_
 }
 
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E) {
-  if (T <= 0 || T > kMaxTokens || H <= 0 || H % 512 != 0 || E <= 0) return 0;
+  if (T <= 0 || T > kMaxTokens || H <= 0 || H % 512 != 0 || H > MOE_MAX_DIM || E <= 0) return 0;
   return static_cast<size_t>(moe::route_hsplit(T, H)) * static_cast<size_t>(T) * static_cast<size_t>(E) * sizeof(double);
 }
 
@@ -88,7 +88,7 @@ int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, co
                                              as_stream(stream)));
   }
   if (!x || !w_router) return MOE_EINVAL;
-  if (H <= 0 || H % 512 != 0) return MOE_ESHAPE;
+  if (H <= 0 || H % 512 != 0 || H > MOE_MAX_DIM) return MOE_ESHAPE;
   if (!aligned(x, 16) || !aligned(w_router, 4)) return MOE_EALIGN;
   if (!ws) return MOE_EINVAL;
   if (!aligned(ws, 256)) return MOE_EALIGN;

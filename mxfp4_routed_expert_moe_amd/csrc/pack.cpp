@@ -16,7 +16,11 @@
 
 namespace {
 
-bool shape_ok(int32_t H, int32_t I) { return H > 0 && I > 0 && H % 512 == 0 && I % 512 == 0; }
+// H and I: positive multiples of 512 up to MOE_MAX_DIM, so every size below
+// fits 64 bits and every tile index an int.
+bool shape_ok(int32_t H, int32_t I) {
+  return H > 0 && I > 0 && H % 512 == 0 && I % 512 == 0 && H <= MOE_MAX_DIM && I <= MOE_MAX_DIM;
+}
 
 // Offset in the tiled nibble plane of canonical byte (n, kb) of an [N, K] projection.
 inline uint64_t tiled_nib_index(int N, int K, int n, int kb) {

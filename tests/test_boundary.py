@@ -165,6 +165,7 @@ def test_pack_affine2_matches_documented_layout_and_round_trips(shape):
     assert L.moe_pack_affine2(canon.ctypes.data, n, 0, H, I, out.ctypes.data, n) == EINVAL
     assert L.moe_pack_affine2(canon.ctypes.data, n, E, H, I, canon.ctypes.data + 16, n) == EINVAL  # overlap
     assert L.moe_expert_bytes_affine2(4096, 2048) == 8_388_608 and L.moe_expert_bytes_affine2(4000, 2048) == 0
+    assert L.moe_expert_bytes_affine2(B.MOE_MAX_DIM + 512, 512) == 0 and L.moe_expert_bytes(512, B.MOE_MAX_DIM + 512) == 0
 
 
 def test_pack_rejects_bad_arguments():

@@ -56,9 +56,10 @@ extern "C" {
  * activation a (x, then h) is carried as two E4M3 terms under one E8M0 scale
  * S per 32 consecutive k:  a = S * hi + (S / 16) * lo.  That is exact for
  * every value within 2^13 of its block's largest magnitude and off by at
- * most 2^-21 of that magnitude below it (the reading of "Model techniques map
- * -- DeepSeek-V4-Flash", row "MXFP4 experts", taken for this option: weights
- * stay MXFP4, activations keep bf16 precision).  Default 0: the weights are
+ * most 2^-21 of that magnitude below it (the reading taken for this option
+ * of "ElytronAI / DeepSeek-v4-Flash", Sizes, where the experts are MXFP4, and
+ * of the activations being bf16: weights stay MXFP4, activations keep bf16
+ * precision).  Default 0: the weights are
  * decoded to bf16 for bf16 matrix cores.  The flag changes the workspace size.
  */
 #define MOE_FFN_SPLIT_FP8 1

@@ -10,8 +10,10 @@
 //   v = S * hi + (S / 16) * lo,   hi = RNE_e4m3(v / S),  lo = RNE_e4m3(16 (v / S - hi)),
 // with S = 2^(floor(log2 max|v|) - 7), so |v| / S < 256 and |lo| <= 128.  hi
 // keeps the top 4 significant bits of v and lo the remaining 4, so the sum is
-// exactly v for every element within 2^14 of the block maximum (all others
-// are off by at most 2^-18 of it).  Each 16x16x128 product is two MFMAs, hi
+// exactly v for every element within 2^13 of the block maximum: there v / S
+// >= 2^-6 and the 4 bits of 16 (v / S - hi) lie on the E4M3 grid.  Smaller
+// elements lose only what falls below the E4M3 subnormal step 2^-9 of lo,
+// S * 2^-14 <= 2^-21 of the block maximum.  Each 16x16x128 product is two MFMAs, hi
 // then lo, at the FP8 rate -- the bf16 rate overall -- and the weights need no
 // conversion instructions at all.
 #include "ffn_internal.h"

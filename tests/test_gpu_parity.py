@@ -165,10 +165,11 @@ def test_identity_experts_closed_form_and_orientation(T, split):
         # Two E4M3 terms under one power-of-two scale per 32 k are exact down
         # to 2^-13 of the block's largest magnitude and off by at most 2^-21
         # of it below that.  For x this moves only |v| < 2^-13 max|x|, where
-        # the SwiGLU slope is about 2|v|; for h it lands on the output as is:
-        # allow 2^-18 of the 32-column block maximum.
+        # the SwiGLU slope is about 2|v|; for h it lands on the output as is
+        # (identity down weights, one product per output): 2^-21 of the
+        # 32-column block maximum.
         blk = np.repeat(np.abs(want).reshape(want.shape[0], I // 32, 32).max(axis=2), 32, axis=1)
-        tol = tol + 2.0 ** -18 * blk
+        tol = tol + 2.0 ** -21 * blk
         # the expert row is rounded to bf16 once more (half an ulp, 2^-9
         # relative), no longer exactly h once the split has moved it
         tol = tol + 2.0 ** -9 * np.abs(rows[:, :I])
@@ -606,3 +607,34 @@ def test_affine2_full_workloads(index, sample):
           f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
     del r, ex
     torch.cuda.empty_cache()
+
+
+# The four calls captured in a HIP graph (the library allocates nothing and
+# issues no memsets) and replayed several times, with eager work and host
+# synchronisation between replays and the outputs cleared to NaN before each:
+# every replay must reproduce the eager layer bit for bit.  Decode and
+# prefill kernel families.
+@pytest.mark.parametrize("T", [37, 300])
+def test_graph_replay_matches_eager(T):
+    print(f"[parity] graph replay T={T}", flush=True)
+    inp = _small_inputs(T, 512, 512, 16, 8100 + T)
+    ex = _experts(inp)
+    g = LC.run_gpu_layer(inp, ex)
+    layer = g["layer"]
+    y_ref = layer.y.clone()
+    rows_ref = layer.out_rows.clone()
+    n = int(g["offsets"][-1])
+    xd = LC.dev(inp.x)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(xd)
+    scratch = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        layer.y.view(torch.uint8).fill_(0xFF)
+        layer.out_rows.view(torch.uint8).fill_(0xFF)
+        scratch.mul_(1.0001)                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(layer.y, y_ref), f"replay {rep}: y differs from the eager layer"
+        assert torch.equal(layer.out_rows[:n], rows_ref[:n]), f"replay {rep}: expert rows differ"

@@ -244,11 +244,21 @@ int moe_unpack_affine2(const uint8_t* src_device_layout, uint64_t src_bytes, int
  * "DeepSeek-V4-Flash export design", Source configuration, MoE bullet).
  *
  * Learned mode (hash_table == NULL):
- *   z[t,e] = sum_h x[t,h] * w_router[h,e]   accumulated in float64
- *   s      = sqrt(softplus(z))              float64
+ *   z[t,e] = sum_h x[t,h] * w_router[h,e]
+ *   s      = sqrt(softplus(z))
  *   ids[t] = the top_k experts by s + sel_bias[e] (sel_bias NULL = 0), in
  *            descending key order, equal keys to the lower expert id
  *   weights[t,j] = route_scale * s[ids[t,j]] / sum_j s[ids[t,j]]  (unbiased s)
+ * The ids are those of the float64 z (sums of exact products, rounded only
+ * in float64 additions).  T <= 256, or E not a multiple of 64, or w_router
+ * not 16-byte aligned: z in float64 for every (t, e).  Otherwise z comes
+ * from the bf16 matrix cores (w_router split exactly into three bf16 terms,
+ * float32 sums of each 32-long k step added in float64) with a bound on its
+ * error; a token whose selection the bound cannot decide gets float64 z, and
+ * chosen experts whose order the bound cannot decide, or whose s is below
+ * sqrt(softplus(4)), get float64 z before ordering and weighting.  The
+ * remaining z carry that rounding (about 1e-6 absolute at |z| ~ 20), which
+ * moves a weight by well under 1e-6 relative.
  * Hash mode (hash_table != NULL): ids[t,j] = hash_table[token_ids[t]*top_k + j]
  *   and weights = route_scale / top_k.  A token id outside [0, V) gives ids -1
  *   for that token (moe_dispatch then drops those pairs).

@@ -56,27 +56,6 @@ __device__ __forceinline__ void window_unit(int lam, int n_items, int nbc, int& 
   cb = cg * gc + r2 % gc;
 }
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
-// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Block barrier for the activation ring.  Unlike __syncthreads() it does not
-// drain the vector-memory counter, so the prefetched tiles stay in flight
-// across it.  No release fence is needed: the only LDS writes are LDS-DMA
-// loads, which each wave has already waited for explicitly (wait_vmcnt), and
-// every LDS read before it has been consumed by an MFMA.  The acquire fence
-// keeps later LDS reads below the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Phase 1 (gateup = true: x rows -> h) or phase 2 (h rows -> out_rows).
 // The decode family reads the dispatch offsets directly; the prefill family
 // walks the work list (grid (column blocks, max_items), surplus blocks return).

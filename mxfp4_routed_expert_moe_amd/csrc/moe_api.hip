@@ -70,7 +70,7 @@ int moe_experts_init(moe_experts* d, const void* base, int32_t n_experts, int32_
 
 size_t moe_route_workspace_size(int32_t T, int32_t H, int32_t E) {
   if (T <= 0 || T > kMaxTokens || H <= 0 || H % 512 != 0 || H > MOE_MAX_DIM || E <= 0) return 0;
-  return static_cast<size_t>(moe::route_hsplit(T, H)) * static_cast<size_t>(T) * static_cast<size_t>(E) * sizeof(double);
+  return moe::route_ws_bytes(T, H, E);
 }
 
 int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, const float* sel_bias,
@@ -93,8 +93,8 @@ int moe_route(const uint16_t* x, int32_t T, int32_t H, const float* w_router, co
   if (!ws) return MOE_EINVAL;
   if (!aligned(ws, 256)) return MOE_EALIGN;
   if (ws_bytes < moe_route_workspace_size(T, H, E)) return MOE_EWORKSPACE;
-  return hip_status(moe::launch_route_learned(x, T, H, w_router, sel_bias, E, top_k, route_scale, ids, weights,
-                                              static_cast<double*>(ws), as_stream(stream)));
+  return hip_status(moe::launch_route_learned(x, T, H, w_router, sel_bias, E, top_k, route_scale, ids, weights, ws,
+                                              as_stream(stream)));
 }
 
 size_t moe_dispatch_workspace_size(int32_t T, int32_t E, int32_t top_k) {

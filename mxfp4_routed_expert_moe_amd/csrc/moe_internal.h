@@ -129,6 +129,28 @@ __device__ __forceinline__ bf16x8 dequant8_fp8(uint32_t lo, uint32_t hi, float s
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
 
+// ---------------------------------------------------------------- pipelines
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |
+// expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Block barrier for the activation ring.  Unlike __syncthreads() it does not
+// drain the vector-memory counter, so the prefetched tiles stay in flight
+// across it.  No release fence is needed: the only LDS writes are LDS-DMA
+// loads, which each wave has already waited for explicitly (wait_vmcnt), and
+// every LDS read before it has been consumed by an MFMA.  The acquire fence
+// keeps later LDS reads below the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------- wave / block scans
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -194,9 +216,9 @@ __device__ inline int block_excl_scan_1024(int* a, int n, int* tmp) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipGetLastError() of its launches.  Arguments are validated
 // by the caller in moe_api.hip.
-int route_hsplit(int T, int H);
+size_t route_ws_bytes(int T, int H, int E);
 hipError_t launch_route_learned(const uint16_t* x, int T, int H, const float* w, const float* bias, int E, int k,
-                                float scale, int32_t* ids, float* weights, double* part, hipStream_t s);
+                                float scale, int32_t* ids, float* weights, void* ws, hipStream_t s);
 hipError_t launch_route_hash(const int32_t* tok, int T, const int32_t* table, int V, int k, float scale,
                              int32_t* ids, float* weights, hipStream_t s);
 

@@ -329,6 +329,51 @@ def test_forced_routing_by_bias(T):
     LC.check_routing(g, ids_ref, w_ref, gap)
 
 
+@pytest.mark.parametrize("T", [300, 5000])
+def test_router_zero_rows_go_to_the_float64_list(T):
+    """Every other token's x row is zero: all its logits are 0, its keys tie,
+    and the matrix-core bound cannot order them, so those tokens (half the
+    batch) are decided on the float64 list: ids 0..5 in order, equal weights.
+    The other tokens are decided as usual."""
+    print(f"[parity] router zero rows T={T}", flush=True)
+    H, E = 1024, 256
+    seed = 7000 + T
+    x = WL.make_x(seed, T, H)
+    x[1::2] = 0
+    router = WL.make_router(seed, H, E)
+    ids_ref, w_ref, _ = O.route_learned(x, router, None, 6, WL.ROUTE_SCALE)
+    gap = O.boundary_gap(x, router, None, 6)
+    ids, wts = B.route(LC.dev(x), T, E, 6, WL.ROUTE_SCALE, w_router=LC.dev(router))
+    torch.cuda.synchronize()
+    g = dict(ids=LC.host(ids), weights=LC.host(wts))
+    z = slice(1, None, 2)
+    assert (ids_ref[z] == np.arange(6)).all()
+    assert np.array_equal(g["ids"][z], ids_ref[z])
+    assert np.array_equal(g["weights"][z], w_ref[z].astype(np.float32))
+    live = np.arange(0, T, 2)
+    sub = dict(ids=g["ids"][live], weights=g["weights"][live])
+    LC.check_routing(sub, ids_ref[live], w_ref[live], gap[live])
+
+
+def test_router_huge_weight_sends_every_token_to_the_float64_list():
+    """A router weight of 2^121 fails the split's range check, so every
+    token's selection comes from the float64 logits; the result must still be
+    the oracle's."""
+    print("[parity] router huge weight", flush=True)
+    T, H, E = 700, 1024, 256
+    seed = 7500
+    x = WL.make_x(seed, T, H)
+    router = WL.make_router(seed, H, E)
+    router[5, 17] = np.float32(2.0 ** 121)
+    ids_ref, w_ref, _ = O.route_learned(x, router, None, 6, WL.ROUTE_SCALE)
+    gap = O.boundary_gap(x, router, None, 6)
+    ids, wts = B.route(LC.dev(x), T, E, 6, WL.ROUTE_SCALE, w_router=LC.dev(router))
+    torch.cuda.synchronize()
+    g = dict(ids=LC.host(ids), weights=LC.host(wts))
+    LC.check_routing(g, ids_ref, w_ref, gap)
+    assert (g["ids"][:, 0] == 17).sum() > T // 3
+
+
 def test_hash_out_of_range_token_gives_dropped_ids():
     E = 16
     table, tok = WL.make_hash(3, 10, E, 6, vocab=50)

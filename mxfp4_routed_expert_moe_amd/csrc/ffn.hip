@@ -69,22 +69,36 @@ inline FfnWs ffn_carve(void* ws, int max_items, int T, int k, int H, int I, bool
 }
 
 // Work list: every group with rows is cut into items of at most bm rows.
+// After the scan of the per-group item counts, thread t writes items t,
+// t + 256, ... (consecutive threads, consecutive 16-byte items), each finding
+// its group by binary search of the item bases in LDS: a hot group's hundreds
+// of items are written by the whole block, not by one thread.
 __global__ __launch_bounds__(256) void ffn_plan_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                        int4* __restrict__ items, int32_t* __restrict__ n_items) {
-  __shared__ int cnt[1024];
+  __shared__ int cnt[1025];
+  __shared__ int off[1025];
   __shared__ int tmp[4];
   const int G = E + 1;
-  for (int g = threadIdx.x; g < G; g += 256) {
-    const int c = offsets[g + 1] - offsets[g];
-    cnt[g] = (c + bm - 1) / bm;
+  for (int g = threadIdx.x; g <= G; g += 256) {
+    off[g] = offsets[g];
+    if (g < G) cnt[g] = (offsets[g + 1] - offsets[g] + bm - 1) / bm;
   }
   __syncthreads();
-  const int total = block_excl_scan_256(cnt, G, tmp);
-  for (int g = threadIdx.x; g < G; g += 256) {
-    const int r0 = offsets[g];
-    const int c = offsets[g + 1] - r0;
-    const int base = cnt[g];
-    for (int i = 0; i * bm < c; ++i) items[base + i] = make_int4(g, r0 + i * bm, min(bm, c - i * bm), 0);
+  const int total = block_excl_scan_256(cnt, G, tmp);  // cnt[g] = first item of group g
+  if (threadIdx.x == 0) cnt[G] = total;
+  __syncthreads();
+  for (int it = threadIdx.x; it < total; it += 256) {
+    // the last group g with cnt[g] <= it (empty groups share their base with the next)
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cnt[mid] <= it) lo = mid;
+      else hi = mid - 1;
+    }
+    const int g = lo;
+    const int i = it - cnt[g];
+    const int c = off[g + 1] - off[g];
+    items[it] = make_int4(g, off[g] + i * bm, min(bm, c - i * bm), 0);
   }
   if (threadIdx.x == 0) *n_items = total;
 }

@@ -149,8 +149,8 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
         launch_ffn_prefill_f8(gateup, gateup ? w.xq : w.hq, rt, w, blob, expert_bytes, H, I, limit, out_rows,
                               max_items, s);
       } else {
-        launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, T, E, shared_w8,
-                           routed_a2, s);
+        launch_ffn_prefill(gateup, act, rt, w, blob, expert_bytes, H, I, limit, out_rows, max_items, T, E, k,
+                           shared_w8, routed_a2, s);
       }
     }
   }

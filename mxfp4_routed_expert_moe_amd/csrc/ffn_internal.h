@@ -64,7 +64,7 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
                        uint16_t* out_rows, bool shared_w8, bool routed_a2, hipStream_t s);
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows, int max_items,
-                        int T, int E, bool shared_w8, bool routed_a2, hipStream_t s);
+                        int T, int E, int k, bool shared_w8, bool routed_a2, hipStream_t s);
 void launch_quant_act(const uint16_t* src, int rows, int K, const QAct& dst, hipStream_t s);
 void launch_ffn_prefill_f8(bool gateup, const QAct& aq, const int32_t* row_token, const FfnWs& w,
                            const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows,

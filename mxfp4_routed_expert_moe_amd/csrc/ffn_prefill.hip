@@ -11,7 +11,6 @@ constexpr int kStages = 4;        // ring depth of activation (LDS) and weight (
 constexpr int kWavesM = 1, kWavesN = 4;        // 4 waves side by side along the columns
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXFP4)
-constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chunks per lane per tile
 
 // grid (n blocks, max items) of 256 threads = 4 waves side by side, two
 // blocks per CU (64 KB of LDS each), so two waves per SIMD: each wave has 4 x 4
@@ -60,15 +59,15 @@ constexpr int kDmaOps = kPrefillRows * 16 / kThreads;  // 16-byte activation chu
 // down) the MFMAs run x against the exact bf16 codes q (P) and against ones
 // (S, the row sums of x over the group), and acc += s * P + b * S -- the
 // group's sum x . (s q + b), regrouped.
-template <bool GATEUP, int FMT>
-__global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
-                                                             const int32_t* __restrict__ row_token,
-                                                             const int4* __restrict__ items,
-                                                             const int32_t* __restrict__ n_items,
-                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
-                                                             int H, int I, float limit, int skip_g, int n_tail,
-                                                             uint16_t* __restrict__ h_out,
-                                                             uint16_t* __restrict__ out_rows) {
+// One block's unit: item (g, row0, nrows) of group g, column block nb, as MT
+// 16-row tiles (MT = 4: the full 64; fewer skip the MFMAs, activation loads and
+// stores of row tiles past the item's rows).  As: the block's activation ring.
+template <bool GATEUP, int FMT, int MT>
+__device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
+                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes, int H, int I,
+                                             float limit, uint16_t* __restrict__ h_out,
+                                             uint16_t* __restrict__ out_rows, int g, int row0, int nrows, int nb,
+                                             uint16_t (*As)[kPrefillRows * 128]) {
   constexpr bool W8 = FMT == kFmtMx8;
   constexpr bool A2 = FMT == kFmtA2;
   constexpr int kNT = kNT4;           // weight n-tiles per wave
@@ -79,20 +78,6 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   constexpr int SPG = G / 32;          // MFMA k steps per affine group
   constexpr uint64_t kSbBytes = 16 * NG * 4;  // affine (scale, bias) words of a 16 x 128 tile
   typedef __attribute__((__vector_size__(NG * sizeof(unsigned)))) unsigned u32xg;
-  __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
-  const int nbc = gridDim.x;
-  const int nit = *n_items;
-  const int total = (n_tail > 0 ? n_tail : nit) * nbc;
-  const int b = blockIdx.x + blockIdx.y * nbc;
-  const int per = (total + 7) >> 3;
-  if ((b >> 3) >= per) return;
-  const int lam = (b & 7) * per + (b >> 3);
-  if (lam >= total) return;
-  int item, nb;
-  window_unit(lam, n_tail > 0 ? n_tail : nit, nbc, item, nb);
-  const int4 it = items[(n_tail > 0 ? nit - n_tail : 0) + item];
-  const int g = it.x, row0 = it.y, nrows = it.z;
-  if (g == skip_g) return;  // this group's items run in a launch of their own
   const int K = GATEUP ? H : I;
   const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
@@ -130,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
 
   // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
-  const char* asrc[kDmaOps];
+  constexpr int kDmaOps = MT;  // 16-byte activation chunks per lane per tile (16 MT rows)
+  const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
 #pragma unroll
   for (int q = 0; q < kDmaOps; ++q) {
     const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
@@ -169,9 +155,9 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
       dst[j] = *reinterpret_cast<const uint32_t*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + grp * 256);
   };
 
-  f32x4 acc[4][kNT];
+  f32x4 acc[MT][kNT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int j = 0; j < kNT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -186,10 +172,10 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
     const uint16_t* abuf = As[st];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 a[4];
+      bf16x8 a[MT];
       const int slot = ((4 * g4 + s) ^ (lane & 15)) * 8;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
+      for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
         // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word
@@ -202,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
           bv = dequant8(bq[sb][j][0][s], scf[j]);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
       }
     }
   };
@@ -215,27 +201,27 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
     const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_w);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      bf16x8 a[SPG][4];
-      f32x4 S[4];
+      bf16x8 a[SPG][MT];
+      f32x4 S[MT];
 #pragma unroll
       for (int ss = 0; ss < SPG; ++ss) {
         const int s = gi * SPG + ss;
         // MFMA step s takes k = 32 s + 8 (lane / 16) + 0..7: 16-byte chunk 4 s + lane / 16 of the row
         const int slot = ((4 * s + g4) ^ (lane & 15)) * 8;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) a[ss][mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
+        for (int mt = 0; mt < MT; ++mt) a[ss][mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ss = 0; ss < SPG; ++ss) S[mt] = mfma16x16x32(a[ss][mt], ones, S[mt]);
       }
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        f32x4 P[4];
+        f32x4 P[MT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) P[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ss = 0; ss < SPG; ++ss) {
           const int s = gi * SPG + ss;
@@ -244,13 +230,13 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
           const uint32_t nib = ((s & 1) ? (w >> 2) : w) & 0x33333333u;
           const bf16x8 bv = dequant8(nib, e8m0_scale_operand(128u));  // scale 2: the bf16 values q
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) P[mt] = mfma16x16x32(a[ss][mt], bv, P[mt]);
+          for (int mt = 0; mt < MT; ++mt) P[mt] = mfma16x16x32(a[ss][mt], bv, P[mt]);
         }
         const uint32_t sbw = sq2[st][j][gi];
         const float sc = __uint_as_float(sbw << 16);          // bf16 scale (low half)
         const float bc = __uint_as_float(sbw & 0xffff0000u);  // bf16 bias (high half)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[mt][j][e] = fmaf(bc, S[mt][e], fmaf(sc, P[mt][e], acc[mt][j][e]));
       }
@@ -306,7 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
           // keep each tile's MFMAs and folds above the next barrier (the
           // compiler otherwise sinks them and runs out of registers)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int j = 0; j < kNT; ++j) asm volatile("" : "+v"(acc[mt][j]));
         } else {
@@ -321,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   }
 
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int rbase = wm * 64 + mt * 16 + 4 * g4;
     if (GATEUP) {
 #pragma unroll
@@ -351,11 +337,53 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   }
 }
 
+// grid (n blocks, max items + kGridSlack) of 256 threads; see above.  SW: a
+// block of an item with fewer than 64 rows runs the unit with ceil(rows / 16)
+// row tiles (a launch option for work lists of many partial items: its
+// register allocation is the largest unit's, and it is chosen on the host).
+template <bool GATEUP, int FMT, bool SW = false>
+__global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const int4* __restrict__ items,
+                                                             const int32_t* __restrict__ n_items,
+                                                             const uint8_t* __restrict__ blob, uint64_t expert_bytes,
+                                                             int H, int I, float limit, int skip_g, int n_tail,
+                                                             uint16_t* __restrict__ h_out,
+                                                             uint16_t* __restrict__ out_rows) {
+  __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
+  const int nbc = gridDim.x;
+  const int nit = *n_items;
+  const int total = (n_tail > 0 ? n_tail : nit) * nbc;
+  const int b = blockIdx.x + blockIdx.y * nbc;
+  const int per = (total + 7) >> 3;
+  if ((b >> 3) >= per) return;
+  const int lam = (b & 7) * per + (b >> 3);
+  if (lam >= total) return;
+  int item, nb;
+  window_unit(lam, n_tail > 0 ? n_tail : nit, nbc, item, nb);
+  const int4 it = items[(n_tail > 0 ? nit - n_tail : 0) + item];
+  const int g = it.x, row0 = it.y, nrows = it.z;
+  if (g == skip_g) return;  // this group's items run in a launch of their own
+#define MOE_UNIT(M) \
+  prefill_unit<GATEUP, FMT, M>(act, row_token, blob, expert_bytes, H, I, limit, h_out, out_rows, g, row0, nrows, nb, As)
+  if constexpr (SW) {
+    switch ((nrows + 15) >> 4) {
+      case 1: MOE_UNIT(1); break;
+      case 2: MOE_UNIT(2); break;
+      case 3: MOE_UNIT(3); break;
+      default: MOE_UNIT(4); break;
+    }
+  } else {
+    MOE_UNIT(4);
+  }
+#undef MOE_UNIT
+}
+
 }  // namespace
 
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows, int max_items,
-                        int T, int E, bool shared_w8, bool routed_a2, hipStream_t s) {
+                        int T, int E, int k, bool shared_w8, bool routed_a2, hipStream_t s) {
   // The routed experts' launch (MXFP4, with an MXFP4 shared expert riding
   // along, or 2-bit affine), then the shared expert's own launch over the last
   // ceil(T / 64) items of the work list when it has another format.
@@ -367,11 +395,18 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   uint16_t* ho = gateup ? w.h : nullptr;
   uint16_t* oo = gateup ? nullptr : out_rows;
   const int32_t* rt = gateup ? row_token : nullptr;
+  // Experts averaging under two items of rows: most items are partial, and
+  // the MXFP4 launch sizes each block to its item's rows (the switch costs
+  // registers, so work lists of mostly full items keep the plain kernel).
+  const bool sw = static_cast<long>(T) * k < 2L * kPrefillRows * E;
 #define MOE_PREFILL(G)                                                                                            \
   do {                                                                                                          \
     if (routed_a2)                                                                                              \
       ffn_prefill_kernel<G, kFmtA2><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I, limit, \
                                                               skip, 0, ho, oo);                                 \
+    else if (sw)                                                                                                \
+      ffn_prefill_kernel<G, kFmtMx4, true><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H,   \
+                                                                     I, limit, skip, 0, ho, oo);                \
     else                                                                                                        \
       ffn_prefill_kernel<G, kFmtMx4><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,      \
                                                                limit, skip, 0, ho, oo);                         \

@@ -236,11 +236,12 @@ def test_ffn_phases_equal_one_call(T):
     assert torch.equal(layer.out_rows[:n], ref[:n])
 
 
-# Learned routing on each logits kernel: up to 256 tokens take the vector-unit
-# kernel; more tokens with 16-byte aligned router weights (E a multiple of 64)
-# take the float64 matrix-core kernel, and the same weights 4 bytes off that
-# alignment the vector-unit kernel.  All must give the oracle's ids bit for bit
-# and its weights, and each other's ids.
+# Learned routing on each logits path: up to 256 tokens take the float64
+# vector-unit kernel; more tokens with 16-byte aligned router weights (E a
+# multiple of 64) take the bf16 matrix-core split path with its bound and
+# float64 list, and the same weights 4 bytes off that alignment the vector-unit
+# kernel.  All must give the oracle's ids bit for bit and its weights, and
+# each other's ids.
 ROUTER_SHAPES = [
     # (T, H, E, bias)
     (3, 512, 16, False),       # a ragged 8-token block, few experts
@@ -249,6 +250,7 @@ ROUTER_SHAPES = [
     (257, 512, 64, True),      # one token past the many-token threshold, ragged 32-token blocks
     (300, 1024, 128, False),
     (1000, 4096, 256, True),   # full hidden size and expert count
+    (600, 1536, 192, True),    # six waves per split-logits block, three k stages per slice
 ]
 
 

@@ -331,7 +331,7 @@ def test_forced_routing_by_bias(T):
     LC.check_routing(g, ids_ref, w_ref, gap)
 
 
-@pytest.mark.parametrize("T", [300, 5000])
+@pytest.mark.parametrize("T", [300, 5000, 20000])   # 20000: 10000 listed tokens, two h slices per listed block
 def test_router_zero_rows_go_to_the_float64_list(T):
     """Every other token's x row is zero: all its logits are 0, its keys tie,
     and the matrix-core bound cannot order them, so those tokens (half the

@@ -141,7 +141,7 @@ hipError_t launch_ffn(const uint16_t* x, int T, const uint8_t* blob, uint64_t ex
       const uint16_t* act = gateup ? x : w.h;
       const int32_t* rt = gateup ? row_token : nullptr;
       if (dec) {
-        launch_ffn_decode(gateup, act, rt, offsets, T, E, blob, expert_bytes, H, I, limit, w.h, out_rows, shared_w8,
+        launch_ffn_decode(gateup, act, rt, offsets, T, E, k, blob, expert_bytes, H, I, limit, w.h, out_rows, shared_w8,
                           routed_a2, s);
       } else if (split) {
         // phase 1 splits x, then writes h split; phase 2 reads it

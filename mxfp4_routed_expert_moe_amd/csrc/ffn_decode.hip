@@ -20,14 +20,18 @@ constexpr int kWaves = 4;  // waves per block; they split the K axis
 // block's LDS for the split-K reduction.  W8: group g is an MXFP8 expert
 // (2048-byte tiles read as two 1 KiB halves; half the n-tiles per block, so
 // the register ring keeps its size).
-template <bool GATEUP, int KTW, bool W8>
+//
+// NARROW (MXFP4): half the n-tiles per block and twice the blocks, for
+// batches so small that only a few experts stream: the launch's blocks then
+// finish more evenly.
+template <bool GATEUP, int KTW, bool W8, bool NARROW = false>
 __device__ __forceinline__ void decode_chunk(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
                                              int g, int row0, int nrows, const uint8_t* __restrict__ blob,
                                              uint64_t expert_bytes, int H, int I, float limit,
                                              uint16_t* __restrict__ h_out, uint16_t* __restrict__ out_rows,
                                              f32x4 (*red)[8][64]) {
   constexpr int KT = kWaves * KTW;    // k tiles of the whole K axis
-  constexpr int NT = W8 ? 4 : 8;      // n-tiles per block (GATEUP: NT/2 gate + NT/2 up)
+  constexpr int NT = W8 || NARROW ? 4 : 8;  // n-tiles per block (GATEUP: NT/2 gate + NT/2 up)
   constexpr int NH = NT / 2;
   constexpr int NQ = W8 ? 2 : 1;      // 16-byte loads per lane per n-tile per k tile
   constexpr uint64_t kTileBytes = W8 ? 2048 : 1024;
@@ -387,7 +391,7 @@ __device__ __forceinline__ void decode_chunk_a2(const uint16_t* __restrict__ act
 // activation loads of a tile are issued one tile ahead and before the weight
 // loads two tiles ahead, so the in-order load counter never makes a tile wait
 // for a later one.
-template <bool GATEUP, int KTW, int FMT>
+template <bool GATEUP, int KTW, int FMT, bool NARROW = false>
 __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16_t* __restrict__ act,
                                                             const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets, int E, int nrouted,
@@ -415,8 +419,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
         decode_chunk<GATEUP, KTW, false>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl, expert_bytes, H,
                                          I, limit, h_out, out_rows, red);
     } else
-      decode_chunk<GATEUP, KTW, FMT == kFmtMx8>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl,
-                                                expert_bytes, H, I, limit, h_out, out_rows, red);
+      decode_chunk<GATEUP, KTW, FMT == kFmtMx8, NARROW>(act, row_token, g, row0, min(kDecodeRows, end - row0), bl,
+                                                        expert_bytes, H, I, limit, h_out, out_rows, red);
   };
   chunk(first, blob);
   // Experts with more than 16 rows (rare while decoding) take further chunks.
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void ffn_decode_kernel(const uint16
 }  // namespace
 
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
-                       int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
+                       int E, int k, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
                        uint16_t* out_rows, bool shared_w8, bool routed_a2, hipStream_t s) {
   const int K = gateup ? H : I;
   const int ktw = K / (128 * kWaves);  // k tiles per wave; decode_k_ok(K) keeps it in {1, 2, 4, 8}
@@ -446,6 +450,11 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
   // in the same launch, an MXFP8 one runs in a launch of its own.
   const dim3 grid(nb, E + (shared_w8 ? 0 : chunks));
   const dim3 grid_sh(nb8, chunks);
+  // MXFP4 gate/up of a batch of at most 64 (token, slot) pairs: the narrow
+  // blocks (measured at 4 tokens: gate/up -3 us; the down projection and
+  // larger batches lose with them)
+  const bool narrow = gateup && !routed_a2 && static_cast<long>(T) * k <= 64;
+  const dim3 grid_n(I / 32, E + (shared_w8 ? 0 : chunks));
   uint16_t* ho = gateup ? h : nullptr;
   uint16_t* oo = gateup ? nullptr : out_rows;
 #define MOE_DECODE_LAUNCH(G, KTW)                                                                                 \
@@ -453,6 +462,9 @@ void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_toke
     if (routed_a2)                                                                                              \
       ffn_decode_kernel<G, KTW, kFmtA2><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, E, blob, eb, H, \
                                                                      I, limit, ho, oo);                         \
+    else if (G && narrow)                                                                                       \
+      ffn_decode_kernel<G, KTW, kFmtMx4, true><<<grid_n, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, E,    \
+                                                                              blob, eb, H, I, limit, ho, oo);   \
     else                                                                                                        \
       ffn_decode_kernel<G, KTW, kFmtMx4><<<grid, 64 * kWaves, 0, s>>>(act, row_token, offsets, E, E, blob, eb,  \
                                                                       H, I, limit, ho, oo);                     \

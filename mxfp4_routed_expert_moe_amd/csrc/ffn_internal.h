@@ -60,7 +60,7 @@ __device__ __forceinline__ void window_unit(int lam, int n_items, int nbc, int& 
 // The decode family reads the dispatch offsets directly; the prefill family
 // walks the work list (grid (column blocks, max_items), surplus blocks return).
 void launch_ffn_decode(bool gateup, const uint16_t* act, const int32_t* row_token, const int32_t* offsets, int T,
-                       int E, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
+                       int E, int k, const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* h,
                        uint16_t* out_rows, bool shared_w8, bool routed_a2, hipStream_t s);
 void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_token, const FfnWs& w,
                         const uint8_t* blob, uint64_t eb, int H, int I, float limit, uint16_t* out_rows, int max_items,

@@ -170,6 +170,19 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
 #pragma unroll
     for (int j = 0; j < kNT; ++j) scf[j] = e8m0_scale_operand_of(sw[j], i);
     const uint16_t* abuf = As[st];
+    // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word s, or
+    // 8 E4M3 codes of words 2 (s % 2), +1 of half s / 2
+    auto conv = [&](int s, int j) -> bf16x8 {
+      if constexpr (W8) {
+        const u32x4& hw = bq[sb][j][s >> 1];
+        return dequant8_fp8(hw[2 * (s & 1)], hw[2 * (s & 1) + 1], scf[j]);
+      } else {
+        return dequant8(bq[sb][j][0][s], scf[j]);
+      }
+    };
+    // The B operand of the next (s, j) group is converted before the current
+    // group's MFMAs are issued, so its conversions overlap them.
+    bf16x8 bcur = conv(0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 a[MT];
@@ -178,17 +191,12 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
       for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const bf16x8*>(abuf + (arow + 16 * mt) * 128 + slot);
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        // k = 32 (lane / 16) + 8 s + 0..7 of the tile: 8 E2M1 codes of word
-        // s, or 8 E4M3 codes of words 2 (s % 2), +1 of half s / 2
-        bf16x8 bv;
-        if constexpr (W8) {
-          const u32x4& hw = bq[sb][j][s >> 1];
-          bv = dequant8_fp8(hw[2 * (s & 1)], hw[2 * (s & 1) + 1], scf[j]);
-        } else {
-          bv = dequant8(bq[sb][j][0][s], scf[j]);
-        }
+        const int ns = j + 1 < kNT ? s : s + 1, nj = j + 1 < kNT ? j + 1 : 0;
+        bf16x8 bnext = bcur;
+        if (ns < 4) bnext = conv(ns, nj);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bv, acc[mt][j]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16x16x32(a[mt], bcur, acc[mt][j]);
+        bcur = bnext;
       }
     }
   };

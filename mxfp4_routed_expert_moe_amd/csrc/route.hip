@@ -404,11 +404,11 @@ __global__ __launch_bounds__(256 * SPLIT) void route_topk_kernel(const double* _
 // finite, the token goes on the float64 list.
 //
 // Weights.  The logits' actual rounding (about 1e-6 at most, not the bound)
-// moves s by a relative sigma(z) / (2 softplus(z)) times it: below 1/16 for
-// z >= 8, up to 1/2 for very negative z, which a selection bias can still
+// moves s by a relative sigma(z) / (2 softplus(z)) times it: below 1/8 for
+// z >= 4, up to 1/2 for very negative z, which a selection bias can still
 // choose.  So the top-k kernel recomputes in float64, from x and a
 // transposed float32 copy of W, every chosen logit whose s is below
-// sqrt(softplus(8)), and takes the weights from those.
+// sqrt(softplus(4)) (kRefineS), and takes the weights from those.
 
 constexpr int kSplitTok = 64;   // tokens per block of the split logits kernel
 constexpr int kSplitStage = 64; // k per pipeline stage

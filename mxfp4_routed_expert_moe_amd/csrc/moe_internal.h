@@ -127,7 +127,10 @@ __device__ __forceinline__ bf16x8 dequant8_fp8(uint32_t lo, uint32_t hi, float s
   return __builtin_bit_cast(bf16x8, w);
 }
 
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + __expf(-v)); }
+// v / (1 + e^-v) from the fast exponential (relative error about |v| 2^-24)
+// and the hardware reciprocal (1 ulp): for the |v| that matter, both far
+// below the bf16 rounding of h that follows (2^-9 relative).
+__device__ __forceinline__ float silu_f(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
 // ---------------------------------------------------------------- pipelines
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt[3:0] |

@@ -21,12 +21,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+// float32 -> bf16 bits, round to nearest even; NaN stays NaN.  One gfx950
+// convert (v_cvt_pk_bf16_f32); on the device it gave the same bits as the
+// integer form (add 0x7fff plus the kept low bit, shift by 16) for all 2^32
+// non-NaN inputs, denormals included.
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // ---------------------------------------------------------------- MXFP4

@@ -63,10 +63,18 @@ def _parse():
     return p.parse_args()
 
 
+KERNEL_HEADERS = ("ffn_internal.h", "moe_internal.h")  # included by every FFN kernel source
+
+
 def source_hash(name: str) -> str:
-    """Short hash of a kernel source file (ffn_decode.hip or ffn_prefill.hip)."""
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Short hash of a kernel source file (ffn_decode.hip, ffn_prefill.hip or
+    ffn_prefill_f8.hip) followed by the headers it includes, so that a change
+    to a shared device helper also retires the counters taken before it."""
+    h = hashlib.sha256()
+    for n in (name,) + KERNEL_HEADERS:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str, source: str):

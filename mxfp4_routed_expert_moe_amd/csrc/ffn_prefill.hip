@@ -81,7 +81,7 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   const int K = GATEUP ? H : I;
   const int KT = K >> 7;  // a multiple of 4
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const ExpertPlanes pl = W8 ? expert_planes8(H, I) : A2 ? expert_planes_a2(H, I) : expert_planes(H, I);
   const uint8_t* eb = blob + static_cast<uint64_t>(g) * expert_bytes;
@@ -107,22 +107,42 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
     sb0 = eb + pl.down_sc + nt0 * sstride;
     sb1 = sb0 + (kNT / 2) * sstride;
   }
-  nb0 += lane * (A2 ? 8 : 16);
-  nb1 += lane * (A2 ? 8 : 16);
+  // The bases above are uniform; a lane adds one 32-bit offset.  MX weight
+  // and scale loads go through one buffer resource per n-tile (its bytes over
+  // all k: at most 1 MiB of codes, 32 KiB of scales), so the k-tile advance is
+  // a scalar offset and the lane offset the only vector operand.
+  const uint32_t loff = lane * (A2 ? 8 : 16);
   // affine: the (scale, bias) words of output column lane % 16 (MFMA result layout)
-  sb0 += A2 ? (lane & 15) * (NG * 4) : lane * 4;
-  sb1 += A2 ? (lane & 15) * (NG * 4) : lane * 4;
+  const uint32_t soff = A2 ? (lane & 15) * (NG * 4) : lane * 4;
+  __amdgpu_buffer_rsrc_t wrc[kNT], src[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    wrc[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>((j < kNT / 2 ? nb0 : nb1) + (j % (kNT / 2)) * tstride),
+                                               0, static_cast<int>(tstride), 0x00020000);
+    src[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>((j < kNT / 2 ? sb0 : sb1) + (j % (kNT / 2)) * sstride),
+                                               0, static_cast<int>(sstride), 0x00020000);
+  }
 
   // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
   constexpr int kDmaOps = MT;  // 16-byte activation chunks per lane per tile (16 MT rows)
+  // Gate/up gathers token rows from anywhere in x (64-bit addresses); the
+  // down projection reads the item's own rows of h through a buffer resource
+  // over them, with 32-bit lane offsets and the k-tile advance scalar.
   const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
+  uint32_t aoff[4];
+  const __amdgpu_buffer_rsrc_t arc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I)), 0, nrows * I * 2, 0x00020000);
 #pragma unroll
   for (int q = 0; q < kDmaOps; ++q) {
     const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
-    const int p = row0 + min(r, nrows - 1);
-    const uint16_t* rowp = GATEUP ? act + static_cast<size_t>(row_token[p]) * H : act + static_cast<size_t>(p) * I;
-    asrc[q] = reinterpret_cast<const char*>(rowp) + 16 * ((lane & 15) ^ (r & 15));
+    const int rr = min(r, nrows - 1);
+    const int p = row0 + rr;
+    const uint32_t cb = 16 * ((lane & 15) ^ (r & 15));
+    if constexpr (GATEUP)
+      asrc[q] = reinterpret_cast<const char*>(act + static_cast<size_t>(row_token[p]) * H) + cb;
+    else
+      aoff[q] = static_cast<uint32_t>(rr) * (I * 2) + cb;
   }
 
   constexpr int kH = kNT / 2;
@@ -134,25 +154,30 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
     if constexpr (A2) {
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        bq2[stage][j] = *reinterpret_cast<const u32x2*>((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes);
-        sq2[stage][j] = *reinterpret_cast<const u32xg*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + kt * kSbBytes);
+        bq2[stage][j] = *reinterpret_cast<const u32x2*>((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes + loff);
+        sq2[stage][j] = *reinterpret_cast<const u32xg*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + kt * kSbBytes + soff);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kNT; ++j)
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-          bq[stage][j][q] = ld16((j < kH ? nb0 : nb1) + (j % kH) * tstride + kt * kTileBytes + q * 1024);
+          bq[stage][j][q] = __builtin_amdgcn_raw_buffer_load_b128(wrc[j], loff, kt * static_cast<int>(kTileBytes) + q * 1024, 0);
     }
 #pragma unroll
-    for (int q = 0; q < kDmaOps; ++q)
-      __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
-                                       0, 0);
+    for (int q = 0; q < kDmaOps; ++q) {
+      if constexpr (GATEUP)
+        __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
+                                         0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arc, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16, aoff[q],
+                                                 kt * 256, 0, 0);
+    }
   };
   auto issue_scales = [&](uint32_t* dst, int grp) {
 #pragma unroll
     for (int j = 0; j < kNT; ++j)
-      dst[j] = *reinterpret_cast<const uint32_t*>((j < kH ? sb0 : sb1) + (j % kH) * sstride + grp * 256);
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b32(src[j], soff, grp * 256, 0);
   };
 
   f32x4 acc[MT][kNT];

@@ -339,34 +339,50 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
     }
   }
 
+  // Epilogue: the block's output tile (64 rows x 128 h columns, or 64 x 256
+  // down columns, bf16) is assembled in the free activation ring, rows
+  // padded by 16 bytes so the 16-row MFMA result columns land on distinct
+  // banks, then written out in 16-byte chunks, whole rows at a time.
+  constexpr int kOutCols = GATEUP ? 16 * kH * kWavesN : 16 * kNT * kWavesN;  // 128 or 256
+  constexpr int kStageLd = kOutCols + 8;                                       // uint16 elements per staged row
+  static_assert(kPrefillRows * kStageLd <= kStages * kPrefillRows * 128, "staged tile fits the ring");
+  uint16_t* stg = &As[0][0];
+  __syncthreads();  // every wave is done with the ring's last tiles
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int rbase = wm * 64 + mt * 16 + 4 * g4;
     if (GATEUP) {
 #pragma unroll
       for (int j = 0; j < kH; ++j) {
-        const int col = nb * (64 * kH) + wn * (16 * kH) + j * 16 + (lane & 15);
+        const int c = wn * (16 * kH) + j * 16 + (lane & 15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = rbase + e;
-          if (r < nrows) {
-            const float gv = fminf(acc[mt][j][e], limit);
-            const float uv = fminf(fmaxf(acc[mt][j + kH][e], -limit), limit);
-            h_out[static_cast<size_t>(row0 + r) * I + col] = float_to_bf16_bits(silu_f(gv) * uv);
-          }
+          const float gv = fminf(acc[mt][j][e], limit);
+          const float uv = fminf(fmaxf(acc[mt][j + kH][e], -limit), limit);
+          stg[(rbase + e) * kStageLd + c] = float_to_bf16_bits(silu_f(gv) * uv);
         }
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kNT; ++j) {
-        const int col = nb * (64 * kNT) + wn * (16 * kNT) + j * 16 + (lane & 15);
+        const int c = wn * (16 * kNT) + j * 16 + (lane & 15);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rbase + e;
-          if (r < nrows) out_rows[static_cast<size_t>(row0 + r) * H + col] = float_to_bf16_bits(acc[mt][j][e]);
-        }
+        for (int e = 0; e < 4; ++e) stg[(rbase + e) * kStageLd + c] = float_to_bf16_bits(acc[mt][j][e]);
       }
     }
+  }
+  __syncthreads();
+  constexpr int kChunks = kOutCols / 8;  // 16-byte chunks per row
+  uint16_t* const dst = GATEUP ? h_out + static_cast<size_t>(row0) * I + nb * kOutCols
+                               : out_rows + static_cast<size_t>(row0) * H + nb * kOutCols;
+  const int ld = GATEUP ? I : H;
+#pragma unroll
+  for (int i = 0; i < (16 * MT * kChunks) / kThreads; ++i) {
+    const int cidx = i * kThreads + tid;
+    const int r = cidx / kChunks, c = cidx % kChunks;
+    if (r < nrows)
+      *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(r) * ld + 8 * c) =
+          *reinterpret_cast<const u32x4*>(stg + r * kStageLd + 8 * c);
   }
 }
 

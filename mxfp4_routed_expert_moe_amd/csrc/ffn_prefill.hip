@@ -62,7 +62,9 @@ constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXF
 // One block's unit: item (g, row0, nrows) of group g, column block nb, as MT
 // 16-row tiles (MT = 4: the full 64; fewer skip the MFMAs, activation loads and
 // stores of row tiles past the item's rows).  As: the block's activation ring.
-template <bool GATEUP, int FMT, int MT>
+// X64: x spans more than 4 GiB, so the MXFP4 gate/up instance gathers its
+// token rows by 64-bit address instead of a 32-bit offset.
+template <bool GATEUP, int FMT, int MT, bool X64>
 __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes, int H, int I,
                                              float limit, uint16_t* __restrict__ h_out,
@@ -126,21 +128,26 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
   // the item reload its last row (never stored).
   constexpr int kDmaOps = MT;  // 16-byte activation chunks per lane per tile (16 MT rows)
-  // Gate/up gathers token rows from anywhere in x (64-bit addresses); the
-  // down projection reads the item's own rows of h through a buffer resource
-  // over them, with 32-bit lane offsets and the k-tile advance scalar.
+  // The down projection reads the item's own rows of h, the MXFP4 gate/up
+  // the token rows it gathers from x (below 4 GiB), each through a buffer
+  // resource, with 32-bit lane offsets and the k-tile advance scalar; the
+  // other gate/up instances gather by 64-bit address.
+  constexpr bool kDma64 = GATEUP && (X64 || FMT != kFmtMx4);
   const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
   uint32_t aoff[4];
   const __amdgpu_buffer_rsrc_t arc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I)), 0, nrows * I * 2, 0x00020000);
+      const_cast<uint16_t*>(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I)), 0, GATEUP ? -1 : nrows * I * 2,
+      0x00020000);
 #pragma unroll
   for (int q = 0; q < kDmaOps; ++q) {
     const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
     const int rr = min(r, nrows - 1);
     const int p = row0 + rr;
     const uint32_t cb = 16 * ((lane & 15) ^ (r & 15));
-    if constexpr (GATEUP)
+    if constexpr (kDma64)
       asrc[q] = reinterpret_cast<const char*>(act + static_cast<size_t>(row_token[p]) * H) + cb;
+    else if constexpr (GATEUP)
+      aoff[q] = static_cast<uint32_t>(row_token[p]) * static_cast<uint32_t>(H * 2) + cb;
     else
       aoff[q] = static_cast<uint32_t>(rr) * (I * 2) + cb;
   }
@@ -166,7 +173,7 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
     }
 #pragma unroll
     for (int q = 0; q < kDmaOps; ++q) {
-      if constexpr (GATEUP)
+      if constexpr (kDma64)
         __builtin_amdgcn_global_load_lds(asrc[q] + kt * 256, &As[stage][((kThreads / 16) * q + 4 * wave) * 128], 16,
                                          0, 0);
       else
@@ -390,7 +397,7 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
 // block of an item with fewer than 64 rows runs the unit with ceil(rows / 16)
 // row tiles (a launch option for work lists of many partial items: its
 // register allocation is the largest unit's, and it is chosen on the host).
-template <bool GATEUP, int FMT, bool SW = false>
+template <bool GATEUP, int FMT, bool SW = false, bool X64 = false>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   const int g = it.x, row0 = it.y, nrows = it.z;
   if (g == skip_g) return;  // this group's items run in a launch of their own
 #define MOE_UNIT(M) \
-  prefill_unit<GATEUP, FMT, M>(act, row_token, blob, expert_bytes, H, I, limit, h_out, out_rows, g, row0, nrows, nb, As)
+  prefill_unit<GATEUP, FMT, M, X64>(act, row_token, blob, expert_bytes, H, I, limit, h_out, out_rows, g, row0, nrows, nb, As)
   if constexpr (SW) {
     switch ((nrows + 15) >> 4) {
       case 1: MOE_UNIT(1); break;
@@ -448,23 +455,32 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   // the MXFP4 launch sizes each block to its item's rows (the switch costs
   // registers, so work lists of mostly full items keep the plain kernel).
   const bool sw = static_cast<long>(T) * k < 2L * kPrefillRows * E;
+  // x beyond 4 GiB: the MXFP4 gate/up instances gather their rows by 64-bit
+  // address (for the down projection X64 = G is the plain instance)
+  const bool x64 = gateup && static_cast<uint64_t>(T) * static_cast<uint64_t>(H) * 2u > 0xffffffffull;
+#define MOE_MX4(G, SW_, GRID, SKIP, NTAIL)                                                                       \
+  do {                                                                                                          \
+    if (x64)                                                                                                    \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, G><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, \
+                                                                      I, limit, SKIP, NTAIL, ho, oo);           \
+    else                                                                                                        \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, false><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob,   \
+                                                                          eb, H, I, limit, SKIP, NTAIL, ho, oo); \
+  } while (0)
 #define MOE_PREFILL(G)                                                                                            \
   do {                                                                                                          \
     if (routed_a2)                                                                                              \
       ffn_prefill_kernel<G, kFmtA2><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I, limit, \
                                                               skip, 0, ho, oo);                                 \
     else if (sw)                                                                                                \
-      ffn_prefill_kernel<G, kFmtMx4, true><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H,   \
-                                                                     I, limit, skip, 0, ho, oo);                \
+      MOE_MX4(G, true, grid, skip, 0);                                                                          \
     else                                                                                                        \
-      ffn_prefill_kernel<G, kFmtMx4><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,      \
-                                                               limit, skip, 0, ho, oo);                         \
+      MOE_MX4(G, false, grid, skip, 0);                                                                         \
     if (shared_w8)                                                                                              \
       ffn_prefill_kernel<G, kFmtMx8><<<grid_sh, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,   \
                                                                   limit, -1, nsh, ho, oo);                      \
     else if (routed_a2)                                                                                         \
-      ffn_prefill_kernel<G, kFmtMx4><<<grid_sh, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,   \
-                                                                  limit, -1, nsh, ho, oo);                      \
+      MOE_MX4(G, false, grid_sh, -1, nsh);                                                                      \
   } while (0)
   if (gateup) {
     MOE_PREFILL(true);
@@ -472,6 +488,7 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
     MOE_PREFILL(false);
   }
 #undef MOE_PREFILL
+#undef MOE_MX4
 }
 
 }  // namespace moe

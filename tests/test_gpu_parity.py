@@ -468,6 +468,26 @@ def test_max_tokens(path):
     torch.cuda.empty_cache()
 
 
+# Activations of more than 4 GiB (T * H * 2 = 2^32: MOE_MAX_TOKENS tokens of
+# H = 8192): the MXFP4 gate/up launch then gathers its token rows by 64-bit
+# address instead of a 32-bit buffer offset.  Hash routing over 16 experts with
+# I = 512 keeps the experts small; every row and output is checked for being
+# written, expert rows and outputs on 6 tokens (at least one past 2^31 bytes
+# into x).
+def test_gateup_activations_beyond_4gib():
+    T, H, I, E = B.MOE_MAX_TOKENS, 8192, 512, 16
+    assert T * H * 2 >= 1 << 32
+    print(f"[parity] activations beyond 4 GiB: T={T} H={H} I={I} E={E}", flush=True)
+    inp = _small_inputs(T, H, I, E, 4242, routing="hash")
+    r = LC.full_check(inp, _experts(inp), sample_tokens=6, seed=13, route_sample=1024)
+    assert r["ambiguous"] == 0
+    assert len(r["tokens"]) > 0 and int(np.max(r["tokens"])) * H * 2 >= 1 << 31
+    print(f"[parity] T={T} H={H}: rows max/mean rel {r['rows_err'][0]:.2e}/{r['rows_err'][1]:.2e}, "
+          f"y max/mean rel {r['y_err'][0]:.2e}/{r['y_err'][1]:.2e}", flush=True)
+    del r, inp
+    torch.cuda.empty_cache()
+
+
 # The prefill expert FFN on the scaled FP4 matrix cores (MOE_FFN_SPLIT_FP8).
 @pytest.mark.parametrize("T,H,I,E", [(300, 512, 512, 16), (700, 512, 512, 256), (200, 1024, 2048, 32)])
 def test_split_fp8_small_shapes(T, H, I, E):

@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -66,14 +67,24 @@ def _parse():
 KERNEL_HEADERS = ("ffn_internal.h", "moe_internal.h")  # included by every FFN kernel source
 
 
+def _code_text(path: str) -> bytes:
+    """A C++ source with its comments and whitespace removed (string literals
+    in these files hold no comment markers)."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text).encode()
+
+
 def source_hash(name: str) -> str:
-    """Short hash of a kernel source file (ffn_decode.hip, ffn_prefill.hip or
-    ffn_prefill_f8.hip) followed by the headers it includes, so that a change
-    to a shared device helper also retires the counters taken before it."""
+    """Short hash of the code of a kernel source file (ffn_decode.hip,
+    ffn_prefill.hip or ffn_prefill_f8.hip) followed by the headers it
+    includes: a change to the code or to a shared device helper retires the
+    counters taken before it, an edit of comments does not."""
     h = hashlib.sha256()
     for n in (name,) + KERNEL_HEADERS:
-        with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(f.read())
+        h.update(_code_text(os.path.join(CSRC, n)))
     return h.hexdigest()[:16]
 
 

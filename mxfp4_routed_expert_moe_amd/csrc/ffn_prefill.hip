@@ -22,12 +22,20 @@ constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXF
 // otherwise 256 down columns (wave wn: 4 n-tiles).
 //
 // Activation tiles (64 rows x 128 k, 16 KB) go from global memory straight
-// into LDS with the LDS-DMA load (global_load_lds_dwordx4) into a ring of
+// into LDS with the LDS-DMA load (buffer_load_dwordx4 ... lds) into a ring of
 // four stages.  Row r of a tile occupies 256 bytes; its 16-byte chunk c sits
 // at slot c ^ (r & 15), so an MFMA fragment read (16 rows, same chunk) hits 16
 // distinct bank groups.  The DMA puts each wave's 64 lanes in 1 KB of
 // contiguous LDS, so the swizzle is applied on the global side: the lane that
 // lands in slot s of row r loads chunk s ^ (r & 15).
+//
+// Addresses stay scalar where they can: weight and scale loads go through one
+// buffer resource per n-tile and the activation DMA through one over x (or
+// over the item's rows of h), so a lane's 32-bit offset is the only vector
+// operand and the k-tile advance is a scalar offset.
+//
+// Epilogue: the output tile is assembled in the activation ring (idle once
+// the k loop is done) and written in 16-byte stores of whole rows.
 //
 // Pipeline, in pairs of k tiles: after the barrier before tiles kt, kt+1
 // (kt even), tiles kt+2 and kt+3 (weights into registers, then activations

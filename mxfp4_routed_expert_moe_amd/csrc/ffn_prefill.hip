@@ -35,7 +35,9 @@ constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXF
 // operand and the k-tile advance is a scalar offset.
 //
 // Epilogue: the output tile is assembled in the activation ring (idle once
-// the k loop is done) and written in 16-byte stores of whole rows.
+// the k loop is done) and written in 16-byte stores of whole rows, marked
+// non-temporal: the rows are read back only by the next launch, and the L2
+// keeps the weight slices and activation rows the XCD's blocks share.
 //
 // Pipeline, in pairs of k tiles: after the barrier before tiles kt, kt+1
 // (kt even), tiles kt+2 and kt+3 (weights into registers, then activations
@@ -396,8 +398,8 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
     const int cidx = i * kThreads + tid;
     const int r = cidx / kChunks, c = cidx % kChunks;
     if (r < nrows)
-      *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(r) * ld + 8 * c) =
-          *reinterpret_cast<const u32x4*>(stg + r * kStageLd + 8 * c);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + r * kStageLd + 8 * c),
+                                  reinterpret_cast<u32x4*>(dst + static_cast<size_t>(r) * ld + 8 * c));
   }
 }
 

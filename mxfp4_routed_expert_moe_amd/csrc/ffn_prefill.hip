@@ -129,10 +129,8 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   __amdgpu_buffer_rsrc_t wrc[kNT], src[kNT];
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
-    wrc[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>((j < kNT / 2 ? nb0 : nb1) + (j % (kNT / 2)) * tstride),
-                                               0, static_cast<int>(tstride), 0x00020000);
-    src[j] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>((j < kNT / 2 ? sb0 : sb1) + (j % (kNT / 2)) * sstride),
-                                               0, static_cast<int>(sstride), 0x00020000);
+    wrc[j] = raw_buffer((j < kNT / 2 ? nb0 : nb1) + (j % (kNT / 2)) * tstride, static_cast<int>(tstride));
+    src[j] = raw_buffer((j < kNT / 2 ? sb0 : sb1) + (j % (kNT / 2)) * sstride, static_cast<int>(sstride));
   }
 
   // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
@@ -145,9 +143,9 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   constexpr bool kDma64 = GATEUP && (X64 || FMT != kFmtMx4);
   const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
   uint32_t aoff[4];
-  const __amdgpu_buffer_rsrc_t arc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I)), 0, GATEUP ? -1 : nrows * I * 2,
-      0x00020000);
+  // (gate/up: the whole of x, whose size the host checked against 4 GiB)
+  const __amdgpu_buffer_rsrc_t arc =
+      raw_buffer(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I), GATEUP ? -1 : nrows * I * 2);
 #pragma unroll
   for (int q = 0; q < kDmaOps; ++q) {
     const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
@@ -179,7 +177,8 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
       for (int j = 0; j < kNT; ++j)
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
-          bq[stage][j][q] = __builtin_amdgcn_raw_buffer_load_b128(wrc[j], loff, kt * static_cast<int>(kTileBytes) + q * 1024, 0);
+          bq[stage][j][q] =
+              __builtin_amdgcn_raw_buffer_load_b128(wrc[j], loff, kt * static_cast<int>(kTileBytes) + q * 1024, 0);
     }
 #pragma unroll
     for (int q = 0; q < kDmaOps; ++q) {

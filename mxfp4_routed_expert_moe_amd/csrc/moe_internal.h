@@ -61,6 +61,15 @@ __device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float scale) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// A raw buffer resource over `bytes` bytes at `base` (a uniform address):
+// stride 0, and descriptor word 3 = 0x00020000, the 32-bit data format that
+// untyped buffer loads and the buffer form of the LDS-DMA expect on gfx9.
+// Loads through it take a 32-bit lane offset and a scalar offset, and reads
+// past `bytes` return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

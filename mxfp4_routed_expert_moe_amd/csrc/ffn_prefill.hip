@@ -12,7 +12,7 @@ constexpr int kWavesM = 1, kWavesN = 4;        // 4 waves side by side along the
 constexpr int kThreads = 64 * kWavesM * kWavesN;
 constexpr int kNT4 = 16 / kWavesN;               // weight n-tiles per wave (MXFP4)
 
-// grid (n blocks, max items) of 256 threads = 4 waves side by side, two
+// grid (column blocks / UPB, max items) of 256 threads = 4 waves side by side, two
 // blocks per CU (64 KB of LDS each), so two waves per SIMD: each wave has 4 x 4
 // MFMA 16x16x32 accumulators plus a four-deep ring of its weight fragments
 // within half the register file, and one block's barriers, pipeline fill and
@@ -78,8 +78,8 @@ template <bool GATEUP, int FMT, int MT, bool X64>
 __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, const int32_t* __restrict__ row_token,
                                              const uint8_t* __restrict__ blob, uint64_t expert_bytes, int H, int I,
                                              float limit, uint16_t* __restrict__ h_out,
-                                             uint16_t* __restrict__ out_rows, int g, int row0, int nrows, int nb,
-                                             uint16_t (*As)[kPrefillRows * 128]) {
+                                             uint16_t* __restrict__ out_rows, int g, int row0, int nrows,
+                                             int nb_first, int nub, uint16_t (*As)[kPrefillRows * 128]) {
   constexpr bool W8 = FMT == kFmtMx8;
   constexpr bool A2 = FMT == kFmtA2;
   constexpr int kNT = kNT4;           // weight n-tiles per wave
@@ -102,6 +102,37 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   // tiles; affine: kSbBytes per k tile)
   const uint64_t sstride = A2 ? static_cast<uint64_t>(KT) * kSbBytes : static_cast<uint64_t>(KT >> 2) * 256;
 
+  // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
+  // the item reload its last row (never stored).
+  constexpr int kDmaOps = MT;  // 16-byte activation chunks per lane per tile (16 MT rows)
+  // The down projection reads the item's own rows of h, the MXFP4 gate/up
+  // the token rows it gathers from x (below 4 GiB), each through a buffer
+  // resource, with 32-bit lane offsets and the k-tile advance scalar; the
+  // other gate/up instances gather by 64-bit address.
+  constexpr bool kDma64 = GATEUP && (X64 || FMT != kFmtMx4);
+  const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
+  uint32_t aoff[4];
+  // (gate/up: the whole of x, whose size the host checked against 4 GiB)
+  const __amdgpu_buffer_rsrc_t arc =
+      raw_buffer(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I), GATEUP ? -1 : nrows * I * 2);
+#pragma unroll
+  for (int q = 0; q < kDmaOps; ++q) {
+    const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
+    const int rr = min(r, nrows - 1);
+    const int p = row0 + rr;
+    const uint32_t cb = 16 * ((lane & 15) ^ (r & 15));
+    if constexpr (kDma64)
+      asrc[q] = reinterpret_cast<const char*>(act + static_cast<size_t>(row_token[p]) * H) + cb;
+    else if constexpr (GATEUP)
+      aoff[q] = static_cast<uint32_t>(row_token[p]) * static_cast<uint32_t>(H * 2) + cb;
+    else
+      aoff[q] = static_cast<uint32_t>(rr) * (I * 2) + cb;
+  }
+
+#pragma unroll 1
+  for (int u = 0; u < nub; ++u) {
+  const int nb = nb_first + u;
+  if (u > 0) __syncthreads();  // the previous unit's copy-out is done with the ring
   const uint8_t* nb0;
   const uint8_t* nb1;
   const uint8_t* sb0;
@@ -131,33 +162,6 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
   for (int j = 0; j < kNT; ++j) {
     wrc[j] = raw_buffer((j < kNT / 2 ? nb0 : nb1) + (j % (kNT / 2)) * tstride, static_cast<int>(tstride));
     src[j] = raw_buffer((j < kNT / 2 ? sb0 : sb1) + (j % (kNT / 2)) * sstride, static_cast<int>(sstride));
-  }
-
-  // LDS-DMA sources: op q of wave w fills rows 16q + 4w + lane/16.  Rows past
-  // the item reload its last row (never stored).
-  constexpr int kDmaOps = MT;  // 16-byte activation chunks per lane per tile (16 MT rows)
-  // The down projection reads the item's own rows of h, the MXFP4 gate/up
-  // the token rows it gathers from x (below 4 GiB), each through a buffer
-  // resource, with 32-bit lane offsets and the k-tile advance scalar; the
-  // other gate/up instances gather by 64-bit address.
-  constexpr bool kDma64 = GATEUP && (X64 || FMT != kFmtMx4);
-  const char* asrc[4];         // (a size that depends on MT here drops the kernel's host stub)
-  uint32_t aoff[4];
-  // (gate/up: the whole of x, whose size the host checked against 4 GiB)
-  const __amdgpu_buffer_rsrc_t arc =
-      raw_buffer(act + (GATEUP ? 0 : static_cast<size_t>(row0) * I), GATEUP ? -1 : nrows * I * 2);
-#pragma unroll
-  for (int q = 0; q < kDmaOps; ++q) {
-    const int r = (kThreads / 16) * q + 4 * wave + (lane >> 4);
-    const int rr = min(r, nrows - 1);
-    const int p = row0 + rr;
-    const uint32_t cb = 16 * ((lane & 15) ^ (r & 15));
-    if constexpr (kDma64)
-      asrc[q] = reinterpret_cast<const char*>(act + static_cast<size_t>(row_token[p]) * H) + cb;
-    else if constexpr (GATEUP)
-      aoff[q] = static_cast<uint32_t>(row_token[p]) * static_cast<uint32_t>(H * 2) + cb;
-    else
-      aoff[q] = static_cast<uint32_t>(rr) * (I * 2) + cb;
   }
 
   constexpr int kH = kNT / 2;
@@ -400,13 +404,17 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
       __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + r * kStageLd + 8 * c),
                                   reinterpret_cast<u32x4*>(dst + static_cast<size_t>(r) * ld + 8 * c));
   }
+  }
 }
 
-// grid (n blocks, max items + kGridSlack) of 256 threads; see above.  SW: a
-// block of an item with fewer than 64 rows runs the unit with ceil(rows / 16)
-// row tiles (a launch option for work lists of many partial items: its
-// register allocation is the largest unit's, and it is chosen on the host).
-template <bool GATEUP, int FMT, bool SW = false, bool X64 = false>
+// grid (n blocks / UPB, max items + kGridSlack) of 256 threads; see above.
+// SW: a block of an item with fewer than 64 rows runs the unit with
+// ceil(rows / 16) row tiles (a launch option for work lists of many partial
+// items: its register allocation is the largest unit's, and it is chosen on
+// the host).  UPB: column blocks a block takes in turn (same item, adjacent
+// column blocks), so the item lookup, the gathered rows' offsets and the
+// block's launch are paid once per UPB units.
+template <bool GATEUP, int FMT, bool SW = false, bool X64 = false, int UPB = 1>
 __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t* __restrict__ act,
                                                              const int32_t* __restrict__ row_token,
                                                              const int4* __restrict__ items,
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
                                                              uint16_t* __restrict__ h_out,
                                                              uint16_t* __restrict__ out_rows) {
   __shared__ __attribute__((aligned(1024))) uint16_t As[kStages][kPrefillRows * 128];
-  const int nbc = gridDim.x;
+  const int nbc = gridDim.x;  // groups of UPB column blocks
   const int nit = *n_items;
   const int total = (n_tail > 0 ? n_tail : nit) * nbc;
   const int b = blockIdx.x + blockIdx.y * nbc;
@@ -430,7 +438,8 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_prefill_kernel(const uint16_t
   const int g = it.x, row0 = it.y, nrows = it.z;
   if (g == skip_g) return;  // this group's items run in a launch of their own
 #define MOE_UNIT(M) \
-  prefill_unit<GATEUP, FMT, M, X64>(act, row_token, blob, expert_bytes, H, I, limit, h_out, out_rows, g, row0, nrows, nb, As)
+  prefill_unit<GATEUP, FMT, M, X64>(act, row_token, blob, expert_bytes, H, I, limit, h_out, out_rows, g, row0, nrows, \
+                                    UPB * nb, UPB, As)
   if constexpr (SW) {
     switch ((nrows + 15) >> 4) {
       case 1: MOE_UNIT(1); break;
@@ -456,7 +465,8 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   const int skip = own_shared ? E : -1;
   const int nsh = (T + kPrefillRows - 1) / kPrefillRows;
   const int ny = max_items + kGridSlack, ny_sh = nsh + kGridSlack;
-  const dim3 grid(gateup ? I / 128 : H / 256, ny), grid_sh(gateup ? I / 128 : H / 256, ny_sh);
+  const int nbc = gateup ? I / 128 : H / 256;  // column blocks (even: I and H are multiples of 512)
+  const dim3 grid(nbc, ny), grid2(nbc / 2, ny), grid2_sh(nbc / 2, ny_sh);
   uint16_t* ho = gateup ? w.h : nullptr;
   uint16_t* oo = gateup ? nullptr : out_rows;
   const int32_t* rt = gateup ? row_token : nullptr;
@@ -467,14 +477,17 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   // x beyond 4 GiB: the MXFP4 gate/up instances gather their rows by 64-bit
   // address (for the down projection X64 = G is the plain instance)
   const bool x64 = gateup && static_cast<uint64_t>(T) * static_cast<uint64_t>(H) * 2u > 0xffffffffull;
+  // The MXFP4 and MXFP8 instances take column blocks in pairs; the affine
+  // ones (whose registers a second unit would overflow) one at a time.
 #define MOE_MX4(G, SW_, GRID, SKIP, NTAIL)                                                                       \
   do {                                                                                                          \
     if (x64)                                                                                                    \
-      ffn_prefill_kernel<G, kFmtMx4, SW_, G><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, \
-                                                                      I, limit, SKIP, NTAIL, ho, oo);           \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, G, 2><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, \
+                                                                         H, I, limit, SKIP, NTAIL, ho, oo);     \
     else                                                                                                        \
-      ffn_prefill_kernel<G, kFmtMx4, SW_, false><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob,   \
-                                                                          eb, H, I, limit, SKIP, NTAIL, ho, oo); \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, false, 2><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, \
+                                                                             eb, H, I, limit, SKIP, NTAIL, ho,  \
+                                                                             oo);                               \
   } while (0)
 #define MOE_PREFILL(G)                                                                                            \
   do {                                                                                                          \
@@ -482,14 +495,14 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
       ffn_prefill_kernel<G, kFmtA2><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I, limit, \
                                                               skip, 0, ho, oo);                                 \
     else if (sw)                                                                                                \
-      MOE_MX4(G, true, grid, skip, 0);                                                                          \
+      MOE_MX4(G, true, grid2, skip, 0);                                                                         \
     else                                                                                                        \
-      MOE_MX4(G, false, grid, skip, 0);                                                                         \
+      MOE_MX4(G, false, grid2, skip, 0);                                                                        \
     if (shared_w8)                                                                                              \
-      ffn_prefill_kernel<G, kFmtMx8><<<grid_sh, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I,   \
-                                                                  limit, -1, nsh, ho, oo);                      \
+      ffn_prefill_kernel<G, kFmtMx8, false, false, 2><<<grid2_sh, kThreads, 0, s>>>(                            \
+          act, rt, w.items, w.n_items, blob, eb, H, I, limit, -1, nsh, ho, oo);                                 \
     else if (routed_a2)                                                                                         \
-      MOE_MX4(G, false, grid_sh, -1, nsh);                                                                      \
+      MOE_MX4(G, false, grid2_sh, -1, nsh);                                                                     \
   } while (0)
   if (gateup) {
     MOE_PREFILL(true);

@@ -477,17 +477,21 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
   // x beyond 4 GiB: the MXFP4 gate/up instances gather their rows by 64-bit
   // address (for the down projection X64 = G is the plain instance)
   const bool x64 = gateup && static_cast<uint64_t>(T) * static_cast<uint64_t>(H) * 2u > 0xffffffffull;
-  // The MXFP4 and MXFP8 instances take column blocks in pairs; the affine
-  // ones (whose registers a second unit would overflow) one at a time.
-#define MOE_MX4(G, SW_, GRID, SKIP, NTAIL)                                                                       \
+  // The MXFP4 and MXFP8 instances take column blocks in pairs, except the
+  // row-tile switching one: its blocks end at different times, and pairs would
+  // spread a window's blocks over twice the column blocks (more L2 misses).
+  // The affine instances (whose registers a second unit would overflow) take
+  // one at a time.
+#define MOE_MX4(G, SW_, UPB_, GRID, SKIP, NTAIL)                                                                 \
   do {                                                                                                          \
     if (x64)                                                                                                    \
-      ffn_prefill_kernel<G, kFmtMx4, SW_, G, 2><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, \
-                                                                         H, I, limit, SKIP, NTAIL, ho, oo);     \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, G, UPB_><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob,  \
+                                                                            eb, H, I, limit, SKIP, NTAIL, ho,   \
+                                                                            oo);                                \
     else                                                                                                        \
-      ffn_prefill_kernel<G, kFmtMx4, SW_, false, 2><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, \
-                                                                             eb, H, I, limit, SKIP, NTAIL, ho,  \
-                                                                             oo);                               \
+      ffn_prefill_kernel<G, kFmtMx4, SW_, false, UPB_><<<GRID, kThreads, 0, s>>>(act, rt, w.items, w.n_items,    \
+                                                                                blob, eb, H, I, limit, SKIP,    \
+                                                                                NTAIL, ho, oo);                 \
   } while (0)
 #define MOE_PREFILL(G)                                                                                            \
   do {                                                                                                          \
@@ -495,14 +499,14 @@ void launch_ffn_prefill(bool gateup, const uint16_t* act, const int32_t* row_tok
       ffn_prefill_kernel<G, kFmtA2><<<grid, kThreads, 0, s>>>(act, rt, w.items, w.n_items, blob, eb, H, I, limit, \
                                                               skip, 0, ho, oo);                                 \
     else if (sw)                                                                                                \
-      MOE_MX4(G, true, grid2, skip, 0);                                                                         \
+      MOE_MX4(G, true, 1, grid, skip, 0);                                                                       \
     else                                                                                                        \
-      MOE_MX4(G, false, grid2, skip, 0);                                                                        \
+      MOE_MX4(G, false, 2, grid2, skip, 0);                                                                     \
     if (shared_w8)                                                                                              \
       ffn_prefill_kernel<G, kFmtMx8, false, false, 2><<<grid2_sh, kThreads, 0, s>>>(                            \
           act, rt, w.items, w.n_items, blob, eb, H, I, limit, -1, nsh, ho, oo);                                 \
     else if (routed_a2)                                                                                         \
-      MOE_MX4(G, false, grid2_sh, -1, nsh);                                                                     \
+      MOE_MX4(G, false, 2, grid2_sh, -1, nsh);                                                                  \
   } while (0)
   if (gateup) {
     MOE_PREFILL(true);

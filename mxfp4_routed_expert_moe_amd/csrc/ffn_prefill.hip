@@ -129,6 +129,9 @@ __device__ __forceinline__ void prefill_unit(const uint16_t* __restrict__ act, c
       aoff[q] = static_cast<uint32_t>(rr) * (I * 2) + cb;
   }
 
+  // One pass per column block nb_first .. nb_first + nub - 1 of the item; the
+  // body (weight addressing, k loop, epilogue) runs to the end of the
+  // function at this indentation.
 #pragma unroll 1
   for (int u = 0; u < nub; ++u) {
   const int nb = nb_first + u;

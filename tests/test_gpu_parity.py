@@ -105,6 +105,14 @@ def test_determinism_bitwise():
     inp2 = _small_inputs(40, 512, 512, 16, 78)
     ex2 = _experts(inp2)
     assert np.array_equal(LC.run_gpu_layer(inp2, ex2)["y"], LC.run_gpu_layer(inp2, ex2)["y"])
+    # mostly full items (T * k >= 128 E): the prefill instance whose blocks
+    # take two column blocks in turn
+    inp3 = _small_inputs(2000, 512, 512, 16, 79)
+    ex3 = _experts(inp3)
+    c = LC.run_gpu_layer(inp3, ex3)
+    d = LC.run_gpu_layer(inp3, ex3)
+    assert np.array_equal(c["y"], d["y"])
+    assert torch.equal(c["out_rows"], d["out_rows"])
 
 
 @pytest.mark.parametrize("T", [3, 200])
